@@ -1,0 +1,411 @@
+"""Pins for the oracle's DiT block, model and guided Euler step.
+
+Each test checks the oracle against something other than itself: a page's
+stated fact (tests/golden), a closed form, an invariant of the definition, a
+special case that reduces to a textbook computation, or brute force with
+pure-Python loops on tiny inputs."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import dit as O
+from oracle import numerics as N
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+SPEC = json.load(open(os.path.join(GOLD, "spec_table.json")))
+
+
+# --------------------------------------------------------------------------- page facts
+
+def test_dims_match_spec_table():
+    d = O.IDEOGRAM4
+    assert d.emb_dim == SPEC["emb_dim"] and d.num_heads == SPEC["num_heads"]
+    assert d.num_heads * d.head_dim == d.emb_dim
+    assert d.intermediate == SPEC["intermediate"] and d.adaln_dim == SPEC["adaln_dim"]
+    assert d.rope_theta == SPEC["rope_theta"] and list(d.mrope_section) == SPEC["mrope_section"]
+    assert sum(d.mrope_section) * 2 == d.rope_dims
+    assert d.latent_ch == SPEC["vae_channels"] * SPEC["patch"] ** 2 == SPEC["latent_channels"]
+    side = 1024 // SPEC["vae_downsample"] // SPEC["patch"]
+    assert [side, side] == SPEC["example_1024_grid"]
+
+
+def test_param_count_is_about_9_3_billion():
+    p = O.param_count(O.IDEOGRAM4, layers=SPEC["num_layers"])
+    assert abs(p / 1e9 - SPEC["params_billion"]) / SPEC["params_billion"] < 0.01
+
+
+def test_text_width_matches_cache_sizes():
+    tc = json.load(open(os.path.join(GOLD, "text_cache.json")))
+    projected = tc["projected_tokens"] * O.IDEOGRAM4.emb_dim * tc["projected_dtype_bytes"]
+    assert projected / 2 ** 20 == pytest.approx(tc["projected_mib"], abs=0.05)
+    raw = tc["raw_layers"] * tc["raw_width"] * 4 / 2 ** 20
+    assert raw == pytest.approx(tc["raw_mib_per_token"], abs=0.001)
+
+
+# --------------------------------------------------------------------------- norms, SiLU
+
+def test_silu_closed_form():
+    x = np.array([0.0, 1.0, -1.0, 30.0, -30.0])
+    s = O.silu(x)
+    assert s[0] == 0.0
+    assert s[1] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert s[2] == pytest.approx(-1.0 / (1.0 + math.e), rel=1e-15)
+    assert s[3] == pytest.approx(30.0, rel=1e-12) and abs(s[4]) < 1e-11
+
+
+def test_rms_normalize_invariants():
+    rng = np.random.default_rng(0)
+    x = rng.normal(0, 3, (5, 64))
+    y = O.rms_normalize(x, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-14)
+    assert np.allclose(O.rms_normalize(7.5 * x, 0.0), y, atol=1e-14)
+    # brute force one row
+    r = x[2]
+    ms = sum(v * v for v in r) / len(r)
+    assert np.allclose(O.rms_normalize(r[None], 1e-6)[0], [v / math.sqrt(ms + 1e-6) for v in r], rtol=1e-14)
+
+
+def test_adaln_scale_minus_one_is_zero_and_rounds_to_bf16():
+    rng = np.random.default_rng(1)
+    x = N.bf16_round(rng.normal(0, 1, (3, 32)))
+    assert np.all(O.adaln_norm(x, -1.0, 1e-6) == 0)
+    h = O.adaln_norm(x, 0.25, 1e-6)
+    assert np.array_equal(N.bf16_round(h), h)
+
+
+# --------------------------------------------------------------------------- FP8 linear
+
+def test_quantize_rows_is_identity_on_representable_rows():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 0x7E, (4, 40)).astype(np.uint8)
+    codes[:, 0] = 0x7E                                # every row reaches 448 -> inv = 1
+    vals = N.e4m3_decode(codes) * np.where(rng.random((4, 40)) < 0.5, -1, 1)
+    q, alpha = O.quantize_rows_e4m3(vals)
+    assert np.all(alpha == 448.0)
+    assert np.array_equal(N.e4m3_decode(q), vals)
+
+
+def test_fp8_linear_brute_force_when_quantisation_is_exact():
+    rng = np.random.default_rng(3)
+    M, K, Nn = 3, 16, 5
+    ac = rng.integers(0, 0x7E, (M, K)).astype(np.uint8)
+    ac[:, 3] = 0x7E
+    a = N.e4m3_decode(ac)
+    wc = rng.integers(0, 256, (Nn, K)).astype(np.uint8)
+    wc[wc == 0x7F] = 0
+    wc[wc == 0xFF] = 0
+    ws = rng.uniform(1e-4, 1e-2, Nn).astype(np.float32)
+    y = O.fp8_linear(a, wc, ws)
+    wv = N.e4m3_decode(wc)
+    for m in range(M):
+        for n in range(Nn):
+            acc = 0.0
+            for k in range(K):
+                acc += a[m, k] * wv[n, k]
+            assert y[m, n] == pytest.approx(acc * float(ws[n]), rel=1e-14)
+
+
+def test_fp8_linear_zero_row_and_power_of_two_scaling():
+    rng = np.random.default_rng(4)
+    a = N.bf16_round(rng.normal(0, 1, (3, 64)))
+    a[1] = 0
+    wc = rng.integers(0, 0x7E, (7, 64)).astype(np.uint8)
+    ws = np.full(7, 1e-3, np.float32)
+    y = O.fp8_linear(a, wc, ws)
+    assert np.all(y[1] == 0)
+    y8 = O.fp8_linear(a * 8.0, wc, ws)                # same codes, alpha x 8
+    assert np.allclose(y8, 8.0 * y, rtol=1e-14, atol=0)
+
+
+def test_fp8_linear_quantisation_error_is_small():
+    """Per-token E4M3 input quantisation keeps the product within a few percent of
+    the exact bf16 product (3 mantissa bits: relative step 2**-4)."""
+    rng = np.random.default_rng(5)
+    a = N.bf16_round(rng.normal(0, 1, (16, 512)))
+    wc = rng.integers(0, 0x7E, (32, 512)).astype(np.uint8) | (rng.integers(0, 2, (32, 512)) << 7).astype(np.uint8)
+    ws = np.full(32, 1e-3, np.float32)
+    y = O.fp8_linear(a, wc, ws)
+    exact = a @ (N.e4m3_decode(wc) * 1e-3).T
+    assert N.rel_l2(y, exact) < 0.05
+
+
+# --------------------------------------------------------------------------- positions, MRoPE
+
+def test_positions_layout_written_out():
+    pos = O.positions(2, 2, 3)
+    want = [(0, 0, 0), (1, 1, 1),
+            (2, 2, 2), (2, 2, 3), (2, 2, 4),
+            (2, 3, 2), (2, 3, 3), (2, 3, 4)]
+    assert [tuple(p) for p in pos] == want
+    assert [tuple(p) for p in O.positions(0, 1, 2)] == [(0, 0, 0), (0, 0, 1)]
+
+
+def test_mrope_angles_closed_form():
+    d = O.IDEOGRAM4
+    ang = O.mrope_angles(np.array([[3, 5, 7]]), d)[0]
+    assert ang[0] == 3.0                           # j = 0: inv_freq 1, axis t
+    assert ang[24] == pytest.approx(5.0 * 5e6 ** (-24 / 64), rel=1e-15)   # first h pair
+    assert ang[44] == pytest.approx(7.0 * 5e6 ** (-44 / 64), rel=1e-15)   # first w pair
+    assert ang[63] == pytest.approx(7.0 / 5e6 ** (63 / 64), rel=1e-15)
+
+
+def _rand_heads(rng, L, H=2):
+    return N.bf16_round(rng.normal(0, 1, (L, H, 256)))
+
+
+def test_mrope_preserves_pair_norms_and_passes_upper_dims():
+    d = O.IDEOGRAM4
+    rng = np.random.default_rng(6)
+    pos = O.positions(4, 3, 3)
+    u = _rand_heads(rng, len(pos))
+    c, s = O.mrope_cos_sin(pos, d)
+    r = O.apply_mrope(u, c, s, d)
+    n0 = u[..., :64] ** 2 + u[..., 64:128] ** 2
+    n1 = r[..., :64] ** 2 + r[..., 64:128] ** 2
+    assert np.allclose(n0, n1, rtol=1e-6)
+    assert np.array_equal(r[..., 128:], u[..., 128:])
+
+
+def test_mrope_position_zero_is_identity():
+    d = O.IDEOGRAM4
+    c, s = O.mrope_cos_sin(np.zeros((1, 3), np.int64), d)
+    u = _rand_heads(np.random.default_rng(7), 1)
+    assert np.array_equal(O.apply_mrope(u, c, s, d), u)
+
+
+def test_mrope_text_scores_depend_only_on_offset():
+    d = O.IDEOGRAM4
+    rng = np.random.default_rng(8)
+    q = rng.normal(0, 1, (1, 1, 256))
+    k = rng.normal(0, 1, (1, 1, 256))
+
+    def score(i, j):
+        ci, si = O.mrope_cos_sin(np.array([[i, i, i]]), d)
+        cj, sj = O.mrope_cos_sin(np.array([[j, j, j]]), d)
+        # fp64 tables for this identity (the fp32 tables round the factors)
+        ai = O.mrope_angles(np.array([[i, i, i]]), d)
+        aj = O.mrope_angles(np.array([[j, j, j]]), d)
+        qi = O.apply_mrope(q, np.cos(ai), np.sin(ai), d)
+        kj = O.apply_mrope(k, np.cos(aj), np.sin(aj), d)
+        return float(np.sum(qi * kj))
+
+    assert score(10, 3) == pytest.approx(score(110, 103), rel=1e-9)
+    assert score(0, 0) == pytest.approx(score(57, 57), rel=1e-9)
+
+
+def test_mrope_only_the_moved_axis_section_changes():
+    d = O.IDEOGRAM4
+    u = _rand_heads(np.random.default_rng(9), 1, 1)
+    base = np.array([[4, 4, 4]])
+    moved = np.array([[4, 4, 9]])                  # change w only
+    r0 = O.apply_mrope(u, *O.mrope_cos_sin(base, d), d)
+    r1 = O.apply_mrope(u, *O.mrope_cos_sin(moved, d), d)
+    diff = np.abs(r0 - r1)[0, 0]
+    changed = np.nonzero(diff > 0)[0]
+    sec_w = set(range(44, 64)) | set(range(108, 128))
+    assert set(changed.tolist()) <= sec_w and len(changed) > 30
+
+
+def test_qk_norm_rope_output_is_bf16_and_unit_rms_before_gamma():
+    d = O.IDEOGRAM4
+    rng = np.random.default_rng(10)
+    pos = O.positions(2, 2, 2)
+    u = _rand_heads(rng, len(pos))
+    c, s = O.mrope_cos_sin(pos, d)
+    out = O.qk_norm_rope(u, np.ones(256), c, s, d)
+    assert np.array_equal(N.bf16_round(out), out)
+    rms = np.sqrt(np.mean(out ** 2, axis=-1))        # rotation keeps the RMS
+    assert np.allclose(rms, 1.0, atol=1e-2)
+
+
+# --------------------------------------------------------------------------- attention
+
+def _brute_attention(q, k, v):
+    L, H, dd = q.shape
+    out = np.zeros_like(q)
+    for h in range(H):
+        for i in range(L):
+            sc = [sum(q[i, h, t] * k[j, h, t] for t in range(dd)) / math.sqrt(dd) for j in range(L)]
+            m = max(sc)
+            e = [math.exp(s - m) for s in sc]
+            z = sum(e)
+            for t in range(dd):
+                out[i, h, t] = sum(e[j] * v[j, h, t] for j in range(L)) / z
+    return out
+
+
+def test_attention_brute_force_tiny():
+    rng = np.random.default_rng(11)
+    for L in (1, 3, 7):
+        q, k, v = (rng.normal(0, 2, (L, 2, 4)) for _ in range(3))
+        assert np.allclose(O.attention(q, k, v), _brute_attention(q, k, v), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(12)
+    L = 9
+    v = rng.normal(0, 1, (L, 1, 8))
+    q = rng.normal(0, 1, (L, 1, 8))
+    k = np.repeat(rng.normal(0, 1, (1, 1, 8)), L, axis=0)        # all keys equal
+    assert np.allclose(O.attention(q, k, v), np.mean(v, axis=0, keepdims=True), atol=1e-14)
+    k = np.zeros((L, 1, 8))
+    k[4, 0, 0] = 1000.0
+    q = np.zeros((L, 1, 8))
+    q[:, 0, 0] = 1.0                                              # one dominant key
+    assert np.allclose(O.attention(q, k, v), v[4][None], atol=1e-12)
+    # row subset equals the full result
+    q = rng.normal(0, 1, (L, 1, 8))
+    k = rng.normal(0, 1, (L, 1, 8))
+    full = O.attention(q, k, v)
+    assert np.array_equal(O.attention(q, k, v, rows=[7, 2]), full[[7, 2]])
+
+
+# --------------------------------------------------------------------------- block
+
+def _tiny_block(rng, fmt="fp8", gate_zero=False, scale_minus_one=False):
+    from oracle.dit import BlockWeights, Fp8Weight, Nf4Weight
+    d = O.TINY
+    D, F = d.emb_dim, d.intermediate
+
+    def w8(n, k):
+        c = rng.integers(0, 0x7E, (n, k)).astype(np.uint8) | (rng.integers(0, 2, (n, k)) << 7).astype(np.uint8)
+        return Fp8Weight(c, np.full(n, 0.02 * 3 / 448, np.float32))
+
+    def w4(n, k):
+        q = rng.integers(0, 16, (n, k))
+        packed = ((q[:, 0::2] << 4) | q[:, 1::2]).astype(np.uint8)
+        return Nf4Weight(packed, rng.uniform(0.04, 0.08, n * k // 64).astype(np.float32), n, k)
+
+    mk = w8 if fmt == "fp8" else w4
+    mod_b = np.zeros(4 * D, np.float32)
+    mod_w = N.bf16_round(rng.normal(0, 0.02, (4 * D, 512)))
+    if gate_zero:
+        mod_w[D:2 * D] = 0
+        mod_w[3 * D:] = 0
+    if scale_minus_one:
+        mod_w[:D] = 0
+        mod_w[2 * D:3 * D] = 0
+        mod_b[:D] = -1
+        mod_b[2 * D:3 * D] = -1
+    return BlockWeights(mk(3 * D, D), mk(D, D), mk(2 * F, D), mk(D, F),
+                        N.bf16_round(1 + rng.normal(0, 0.02, 256)), N.bf16_round(1 + rng.normal(0, 0.02, 256)),
+                        mod_w, mod_b)
+
+
+def test_block_gate_zero_is_identity():
+    rng = np.random.default_rng(13)
+    w = _tiny_block(rng, gate_zero=True)
+    T, gh, gw = 3, 2, 3
+    x = N.bf16_round(rng.normal(0, 1, (1, T + gh * gw, 512)))
+    c = rng.normal(0, 1, (1, 512))
+    assert np.array_equal(O.block_forward(x, c, w, T, gh, gw, O.TINY), x)
+
+
+def test_block_scale_minus_one_is_identity():
+    """scale = -1 zeroes both normalised inputs; a zero row quantises to zero, so
+    both branches add exactly zero whatever the gates."""
+    rng = np.random.default_rng(14)
+    w = _tiny_block(rng, scale_minus_one=True)
+    x = N.bf16_round(rng.normal(0, 1, (1, 2 + 4, 512)))
+    c = rng.normal(0, 1, (1, 512))
+    assert np.array_equal(O.block_forward(x, c, w, 2, 2, 2, O.TINY), x)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nf4"])
+def test_block_batch_and_row_subset_consistency(fmt):
+    rng = np.random.default_rng(15)
+    w = _tiny_block(rng, fmt)
+    T, gh, gw = 2, 2, 3
+    L = T + gh * gw
+    x = N.bf16_round(rng.normal(0, 1, (2, L, 512)))
+    c = rng.normal(0, 1, (2, 512))
+    both = O.block_forward(x, c, w, T, gh, gw, O.TINY)
+    for b in range(2):
+        one = O.block_forward(x[b:b + 1], c[b:b + 1], w, T, gh, gw, O.TINY)
+        assert np.array_equal(one[0], both[b])
+    rows = [L + 3, 1, 5]
+    sub = O.block_forward(x, c, w, T, gh, gw, O.TINY, rows=rows)
+    assert np.array_equal(sub, both.reshape(2 * L, 512)[rows])
+    assert np.array_equal(N.bf16_round(both), both)
+    assert np.all(np.isfinite(both)) and not np.array_equal(both, x)
+
+
+# --------------------------------------------------------------------------- model / Euler
+
+def test_timestep_embedding_closed_form():
+    e = O.timestep_embedding([0.0, 1.0])
+    assert np.array_equal(e[0, :256], np.ones(256)) and np.array_equal(e[0, 256:], np.zeros(256))
+    assert e[1, 0] == pytest.approx(math.cos(1000.0)) and e[1, 256] == pytest.approx(math.sin(1000.0))
+    assert e[1, 255] == pytest.approx(math.cos(1000.0 * 10000 ** (-255 / 256)))
+
+
+def test_euler_cfg_closed_forms():
+    rng = np.random.default_rng(16)
+    z = rng.integers(-50, 50, (4, 8)).astype(np.float64)
+    vc = rng.integers(-8, 8, (4, 8)).astype(np.float64)
+    vu = rng.integers(-8, 8, (4, 8)).astype(np.float64)
+    z2, v = O.euler_cfg(z, vc, vu, 1.0, 0.25)
+    assert np.array_equal(v, vc) and np.array_equal(z2, z + 0.25 * vc)
+    _, v0 = O.euler_cfg(z, vc, vu, 0.0, 0.25)
+    assert np.array_equal(v0, vu)
+    _, vs = O.euler_cfg(z, vu, vu, 4.0, 0.25)
+    assert np.array_equal(vs, vu)
+    z3, v4 = O.euler_cfg(z, vc, vu, 4.0, 2.0 ** -5)
+    for i in range(4):
+        for j in range(8):
+            vv = vu[i, j] + 4.0 * (vc[i, j] - vu[i, j])
+            assert z3[i, j] == z[i, j] + vv / 32.0       # exact: integers and a power-of-two step
+    # constant velocity integrates exactly over repeated steps of 2**-4
+    zz = z.copy()
+    for _ in range(16):
+        zz, _ = O.euler_cfg(zz, vc, vc, 4.0, 2.0 ** -4)
+    assert np.array_equal(zz, z + vc)
+
+
+def _tiny_model(rng, layers=2):
+    from oracle.dit import ModelWeights
+    D = 512
+    return ModelWeights(
+        blocks=[_tiny_block(rng) for _ in range(layers)],
+        x_w=N.bf16_round(rng.normal(0, 128 ** -0.5, (D, 128))), x_b=rng.normal(0, 0.02, D).astype(np.float32),
+        t_w1=N.bf16_round(rng.normal(0, 512 ** -0.5, (512, 512))), t_b1=rng.normal(0, 0.02, 512).astype(np.float32),
+        t_w2=N.bf16_round(rng.normal(0, 512 ** -0.5, (512, 512))), t_b2=rng.normal(0, 0.02, 512).astype(np.float32),
+        f_mod_w=N.bf16_round(rng.normal(0, 0.02, (D, 512))), f_mod_b=np.zeros(D, np.float32),
+        f_w=N.bf16_round(rng.normal(0, D ** -0.5, (128, D))), f_b=rng.normal(0, 0.02, 128).astype(np.float32))
+
+
+def test_model_velocity_zero_layers_reduces_to_final_layer_of_embedding():
+    rng = np.random.default_rng(17)
+    mw = _tiny_model(rng, layers=0)
+    z = rng.normal(0, 1, (1, 6, 128))
+    text = N.bf16_round(rng.normal(0, 1, (1, 3, 512)))
+    v = O.model_velocity(text, z, [0.3], mw, 2, 3, O.TINY)
+    v_u = O.model_velocity(None, z, [0.3], mw, 2, 3, O.TINY)
+    # with no blocks the text prefix cannot reach the image tokens
+    assert np.array_equal(v, v_u)
+    # textbook composition of the three linear maps, written with explicit loops for one token
+    c = O.timestep_mlp([0.3], mw)[0]
+    xi = N.bf16_round(z[0, 4] @ np.asarray(mw.x_w).T + mw.x_b)
+    sf = O.silu(c) @ np.asarray(mw.f_mod_w).T
+    r = math.sqrt(sum(t * t for t in xi) / 512 + 1e-6)
+    hf = N.bf16_round(np.array([xi[i] / r * (1 + sf[i]) for i in range(512)]))
+    want = np.array([sum(hf[i] * mw.f_w[o, i] for i in range(512)) + mw.f_b[o] for o in range(128)])
+    assert np.allclose(v[0, 4], want, rtol=1e-12, atol=1e-12)
+
+
+def test_cfg_step_uncond_ignores_text_and_guidance_one_gives_cond():
+    rng = np.random.default_rng(18)
+    cond, unc = _tiny_model(rng, 1), _tiny_model(rng, 1)
+    z = rng.normal(0, 1, (1, 4, 128))
+    t1 = N.bf16_round(rng.normal(0, 1, (1, 2, 512)))
+    t2 = N.bf16_round(rng.normal(0, 1, (1, 2, 512)))
+    _, _, vc1, vu1 = O.cfg_step(t1, z, [0.6], 0.125, 4.0, cond, unc, 2, 2, O.TINY)
+    _, _, vc2, vu2 = O.cfg_step(t2, z, [0.6], 0.125, 4.0, cond, unc, 2, 2, O.TINY)
+    assert np.array_equal(vu1, vu2) and not np.array_equal(vc1, vc2)
+    z1, v1, _, _ = O.cfg_step(t1, z, [0.6], 0.125, 1.0, cond, unc, 2, 2, O.TINY)
+    assert np.allclose(v1, vc1, rtol=1e-15, atol=0)
+    assert np.allclose(z1, z + 0.125 * vc1, rtol=1e-15, atol=1e-15)
