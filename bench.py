@@ -1,0 +1,208 @@
+"""Benchmark: one guided Euler flow-matching step of the 34-layer Ideogram-4
+shaped DiT at 1024x1024 on one MI355X (conditional pass on 512 text + 4096
+image tokens, separate image-only unconditional pass on 4096 tokens, CFG 4.0).
+
+Prints ONE JSON line.  `value` is DiT block tokens/s over the whole step
+(34 * (4608 + 4096) block-token passes per step).  The step's TFLOP/s and
+fraction of the FP8 matrix peak, the single-block figures at the other
+workload shapes, the roofline of the dominant kernel (the FP8 gate/up SwiGLU
+projection) and the CPU oracle baseline are reported beside it.
+
+Inputs are synthetic and seeded (weights FP8 E4M3 from N(0, 0.02), latent and
+text N(0, 1), t from the logit-normal draw); all of them are resident in HBM
+before the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak (datasheet)
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def block_flops(L, B, D=4608, F=12288):
+    """Algorithmic FLOPs of one block: 2*(4D^2 + 3DF) per token for the four
+    projections, 4*L^2*D per sequence for attention."""
+    return B * L * 2 * (4 * D * D + 3 * D * F) + B * 4 * L * L * D
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the single-block workloads")
+    ap.add_argument("--cpu-sample", default="block_1024", help="workload timed on the CPU oracle")
+    return ap.parse_args()
+
+
+def time_gpu(fn, iters, warmup=1):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters / 1e3   # seconds per call
+
+
+def cfg_step_bench(sfm, synth, ctx, steps, warmup):
+    import torch
+    w = synth.WORKLOADS["cfg_step_1024"]
+    cond = synth.model_params(w.shape, w.layers, (0, "cond"), device="cuda")
+    unc = synth.model_params(w.shape, w.layers, (0, "uncond"), device="cuda")
+    text, z, t, dt = synth.step_inputs(w, device="cuda")
+    cm, um = sfm.ModelWeights(cond), sfm.ModelWeights(unc)
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw))
+    zo = torch.empty_like(z)
+
+    def step():
+        sfm.sfm_cfg_step(ctx, cm, um, text, z, zo, t, dt, 4.0, w.B, w.T, w.gh, w.gw, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    ok = bool(torch.isfinite(zo).all())
+    del cond, unc, cm, um, ws
+    torch.cuda.empty_cache()
+    return sec, ok
+
+
+def block_bench(sfm, synth, ctx, name, iters=5):
+    import torch
+    w = synth.WORKLOADS[name]
+    p = synth.block_params(w.shape, (0, w.name), w.wfmt, device="cuda")
+    bw = sfm.BlockWeights(p)
+    x, c = synth.block_inputs(w, device="cuda")
+    xo = torch.empty_like(x)
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw, bw.fmt))
+    sec = time_gpu(lambda: sfm.sfm_block_forward(ctx, bw, x, xo, c, w.B, w.T, w.gh, w.gw, ws), iters)
+    fl = block_flops(w.L, w.B)
+    peak = FP8_PEAK_TFLOPS if w.wfmt == "fp8" else BF16_PEAK_TFLOPS
+    return {"workload": w.describe, "ms": round(sec * 1e3, 4), "tokens_per_s": round(w.B * w.L / sec, 1),
+            "tflops": round(fl / sec / 1e12, 2), "frac_matrix_peak": round(fl / sec / 1e12 / peak, 4),
+            "weights": w.wfmt}
+
+
+def gemm_roofline(sfm, synth, ctx, iters=20):
+    """Dominant kernel: the FP8 gate/up projection with the SwiGLU epilogue at
+    the conditional 1024^2 shape (M 4608, N 2 x 12288, K 4608), the largest
+    single launch of the step.  Timed with HIP events on the launch stream."""
+    import torch
+    M, K, F = 4608, 4608, 12288
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randint(0, 0x7E, (M, K), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    sa = torch.full((M,), 1e-3, device="cuda")
+    wq, wsc = synth.fp8_weight(2 * F, K, ("roof",), device="cuda")
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, wq, wsc)
+    out = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    sec = time_gpu(lambda: sfm.sfm_linear(ctx, sfm.SFM_EPI_SWIGLU, a, sa, w, out, M=M, L=M), iters, warmup=3)
+    flops = 2.0 * M * K * 2 * F
+    achieved = flops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "gemm_fp8_kernel (SwiGLU epilogue), M 4608 N 24576 K 4608",
+            "avg_launch_us": round(sec * 1e6, 2), "flop_per_launch": flops}
+
+
+def cpu_baseline(sample):
+    """The CPU oracle (float64 NumPy) on one full-width block of the step's
+    conditional shape: 4608 tokens through one block.  Scaled to block tokens/s."""
+    import numpy as np
+    import torch
+    from oracle import dit as O
+    from stream_flow_matching_amd import synth
+    from tests._util import np64, oracle_block
+    w = synth.WORKLOADS[sample]
+    p = synth.block_params(w.shape, (0, w.name), w.wfmt)
+    x, c = synth.block_inputs(w)
+    ob = oracle_block(p)
+    xx, cc = np64(x), c.numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    O.block_forward(xx, cc, ob, w.T, w.gh, w.gw, O.IDEOGRAM4)
+    sec = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=cores) or cores
+    except Exception:
+        pass
+    return {"value": round(w.B * w.L / sec, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one block of {w.describe}, float64 oracle, {sec:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from stream_flow_matching_amd import sfm, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    ctx = sfm.Context("ideogram4", 0)
+
+    w = synth.WORKLOADS["cfg_step_1024"]
+    sec, ok = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup)
+    tokens = w.layers * (w.B * (w.T + w.gh * w.gw) + w.B * w.gh * w.gw)
+    flops = w.layers * (block_flops(w.T + w.gh * w.gw, w.B) + block_flops(w.gh * w.gw, w.B))
+    step_tflops = flops / sec / 1e12
+    roof = gemm_roofline(sfm, synth, ctx)
+    extra = {}
+    if not args.no_extra:
+        for name in ("block_1024", "block_2048", "block_6to1_nf4"):
+            extra[name] = block_bench(sfm, synth, ctx, name)
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample)
+
+    line = {
+        "metric": "DiT block tokens/s + TFLOP/s (% FP8 MFMA peak) at 1024^2; s per CFG step",
+        "value": round(tokens / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "s_per_cfg_step": round(sec, 5),
+        "step_tflops": round(step_tflops, 2),
+        "step_frac_fp8_peak": round(step_tflops / FP8_PEAK_TFLOPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 matmul (fp32 accumulate), bf16 activations and attention",
+        "data": "synthetic",
+        "finite": ok,
+        "config": {"workload": "cfg_step_1024: " + w.describe, "batch": w.B, "text_tokens": w.T,
+                   "image_grid": [w.gh, w.gw], "layers": w.layers, "weight_sets": 2, "guidance": 4.0,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "blocks": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,626 @@
+// C ABI of the library: argument checking, context set-up (constant tables),
+// workspace planning and the launch sequences of the block, the velocity model
+// and the guided Euler step.  Every check runs before the first enqueue.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "sfm_internal.h"
+
+using namespace sfm;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define SFM_TRY_HIP(expr)                                                                           \
+    do {                                                                                            \
+        hipError_t e_ = (expr);                                                                     \
+        if (e_ != hipSuccess) return fail(SFM_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_));    \
+    } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+    if (!p) return fail(SFM_E_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(SFM_E_ALIGN, "%s is not 16-byte aligned", name);
+    return SFM_OK;
+}
+
+#define SFM_CHECK(expr)            \
+    do {                           \
+        int s_ = (expr);           \
+        if (s_ != SFM_OK) return s_; \
+    } while (0)
+
+int check_dims(const sfm_dims* d) {
+    if (!d) return fail(SFM_E_INVALID_ARG, "dims is NULL");
+    if (d->head_dim != 256 || d->num_heads < 1 || d->emb_dim != d->num_heads * 256)
+        return fail(SFM_E_SHAPE, "need head_dim 256 and emb_dim = num_heads * 256");
+    if (d->rope_dims != 128 || d->mrope_section[0] + d->mrope_section[1] + d->mrope_section[2] != 64 ||
+        d->mrope_section[0] < 0 || d->mrope_section[1] < 0 || d->mrope_section[2] < 0 ||
+        (d->mrope_section[0] & 1) || (d->mrope_section[1] & 1))
+        return fail(SFM_E_SHAPE, "need rope_dims 128 and even mrope sections summing to 64");
+    if (d->intermediate <= 0 || d->intermediate % 256)
+        return fail(SFM_E_SHAPE, "intermediate must be a positive multiple of 256");
+    if (d->adaln_dim <= 0 || d->adaln_dim % 8 || d->adaln_dim > 2048)
+        return fail(SFM_E_SHAPE, "adaln_dim must be a multiple of 8 in [8, 2048]");
+    if (d->latent_ch <= 0 || d->latent_ch % 8) return fail(SFM_E_SHAPE, "latent_ch must be a multiple of 8");
+    if (d->max_text < 0 || d->max_text > 2048) return fail(SFM_E_SHAPE, "max_text must be in [0, 2048]");
+    if (!(d->rope_theta > 1.0f) || !(d->eps > 0.0f)) return fail(SFM_E_INVALID_ARG, "rope_theta / eps invalid");
+    return SFM_OK;
+}
+
+int shape_check(const sfm_dims* d, int B, int T, int gh, int gw) {
+    if (B < 1 || B > 8) return fail(SFM_E_SHAPE, "batch %d outside [1, 8]", B);
+    if (T < 0 || T > d->max_text) return fail(SFM_E_SHAPE, "text length %d outside [0, %d]", T, d->max_text);
+    if (gh < 16 || gw < 16 || gh > 128 || gw > 128)
+        return fail(SFM_E_SHAPE, "image grid %dx%d outside [16, 128] per side (256-2048 px)", gh, gw);
+    if (std::max(gh, gw) > 6 * std::min(gh, gw)) return fail(SFM_E_SHAPE, "aspect ratio of %dx%d above 6:1", gh, gw);
+    return SFM_OK;
+}
+
+// Standard normal quantile: a rational first guess refined by Newton steps on
+// 0.5 * erfc(-x / sqrt(2)) - p, which converge to double precision.
+double normal_quantile(double p) {
+    double x;
+    const double q = p - 0.5;
+    if (fabs(q) < 0.425) {
+        x = q * 2.5066282746310002;  // sqrt(2 pi): first-order guess near the centre
+    } else {
+        const double r = sqrt(-2.0 * log(q < 0 ? p : 1.0 - p));
+        x = (q < 0 ? -1.0 : 1.0) * (r - (2.30753 + 0.27061 * r) / (1.0 + r * (0.99229 + 0.04481 * r)));
+    }
+    for (int it = 0; it < 50; ++it) {
+        const double f = 0.5 * erfc(-x / sqrt(2.0)) - p;
+        const double dens = exp(-0.5 * x * x) / 2.5066282746310002;
+        const double step = f / dens;
+        x -= step;
+        if (fabs(step) < 1e-17 * std::max(1.0, fabs(x))) break;
+    }
+    return x;
+}
+
+// NF4 levels: normal quantiles at evenly spaced probabilities from delta to
+// 1/2 (8 positive, 7 negative) plus zero, scaled so the extremes are +-1.
+void build_nf4_codebook(float out[16]) {
+    const double delta = 0.5 * ((1.0 - 1.0 / 32.0) + (1.0 - 1.0 / 30.0));
+    std::vector<double> v;
+    for (int i = 0; i < 8; ++i) v.push_back(normal_quantile(delta + (0.5 - delta) * i / 8.0));
+    for (int i = 0; i < 7; ++i) v.push_back(-normal_quantile(delta + (0.5 - delta) * i / 7.0));
+    v.push_back(0.0);
+    std::sort(v.begin(), v.end());
+    double top = 0;
+    for (double x : v) top = std::max(top, fabs(x));
+    for (int i = 0; i < 16; ++i) out[i] = (float)(v[i] / top);
+}
+
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* p) : base((char*)p) {}
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + 255) & ~(size_t)255;
+        T* p = base ? (T*)(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+struct BlockWs {
+    float* mod;
+    uint8_t* hq;
+    uint16_t* h;
+    float* hs;
+    uint16_t* qkv;  // also s
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* vt;
+    uint16_t* o;
+    uint8_t* oq;  // also sq
+    float* os;    // also ss
+    size_t bytes;
+};
+
+BlockWs plan_block(const sfm_dims* d, int B, int T, int gh, int gw, int wfmt, void* base) {
+    const int64_t L = T + (int64_t)gh * gw, M = B * L, D = d->emb_dim, F = d->intermediate;
+    const int64_t Lp = padded_len((int)L), H = d->num_heads;
+    Carve c(base);
+    BlockWs w{};
+    w.mod = c.take<float>(B * 4 * D);
+    if (wfmt == SFM_W_FP8_E4M3) {
+        w.hq = c.take<uint8_t>(M * D);
+        w.hs = c.take<float>(M);
+    } else {
+        w.h = c.take<uint16_t>(M * D);
+    }
+    w.qkv = c.take<uint16_t>(std::max(M * 3 * D, M * F));
+    const int64_t hv = B * H * Lp * 256;
+    w.q = c.take<uint16_t>(hv);
+    w.k = c.take<uint16_t>(hv);
+    w.vt = c.take<uint16_t>(hv);
+    w.o = c.take<uint16_t>(M * D);
+    if (wfmt == SFM_W_FP8_E4M3) {
+        w.oq = c.take<uint8_t>(std::max(M * D, M * F));
+        w.os = c.take<float>(M);
+    }
+    w.bytes = c.off + 256;
+    return w;
+}
+
+int check_qweight(const sfm_qweight* w, int fmt, int n, int k, const char* name) {
+    if (!w) return fail(SFM_E_INVALID_ARG, "%s is NULL", name);
+    if (w->fmt != fmt) return fail(SFM_E_INVALID_ARG, "%s: format %d, expected %d", name, w->fmt, fmt);
+    if (w->n != n || w->k != k) return fail(SFM_E_SHAPE, "%s: shape [%d][%d], expected [%d][%d]", name, w->n, w->k, n, k);
+    SFM_CHECK(check_ptr(w->q, name));
+    SFM_CHECK(check_ptr(w->scale, name));
+    return SFM_OK;
+}
+
+int check_block_weights(const sfm_dims* d, const sfm_block_weights* w, int* fmt_out) {
+    if (!w) return fail(SFM_E_INVALID_ARG, "block weights are NULL");
+    const int fmt = w->qkv.fmt;
+    if (fmt != SFM_W_FP8_E4M3 && fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format %d", fmt);
+    const int D = d->emb_dim, F = d->intermediate;
+    SFM_CHECK(check_qweight(&w->qkv, fmt, 3 * D, D, "qkv"));
+    SFM_CHECK(check_qweight(&w->o, fmt, D, D, "o"));
+    SFM_CHECK(check_qweight(&w->gate_up, fmt, 2 * F, D, "gate_up"));
+    SFM_CHECK(check_qweight(&w->down, fmt, D, F, "down"));
+    SFM_CHECK(check_ptr(w->q_norm, "q_norm"));
+    SFM_CHECK(check_ptr(w->k_norm, "k_norm"));
+    SFM_CHECK(check_ptr(w->mod_w, "mod_w"));
+    SFM_CHECK(check_ptr(w->mod_b, "mod_b"));
+    *fmt_out = fmt;
+    return SFM_OK;
+}
+
+hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa, const sfm_qweight* w, uint16_t* out,
+                const uint16_t* resid, const float* gate, int64_t gs, int M, int L, hipStream_t st) {
+    if (w->fmt == SFM_W_FP8_E4M3)
+        return launch_gemm_fp8(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, w->scale, out, resid, gate, gs, M,
+                               w->n, w->k, L, st);
+    Nf4Code code;
+    memcpy(code.v, ctx->nf4_code, sizeof code.v);
+    return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, w->scale, code, out, resid, gate, gs, M,
+                           w->n, w->k, L, st);
+}
+
+#define SFM_LAUNCH(expr)                                                                              \
+    do {                                                                                              \
+        hipError_t e_ = (expr);                                                                       \
+        if (e_ != hipSuccess) return fail(SFM_E_DEVICE, "launch %s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+// Enqueue one block; arguments already checked.
+int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
+              const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st) {
+    const sfm_dims* d = &ctx->dims;
+    const int L = T + gh * gw, M = B * L, D = d->emb_dim, F = d->intermediate, H = d->num_heads;
+    const int64_t ms = 4 * (int64_t)D;
+    BlockWs b = plan_block(d, B, T, gh, gw, fmt, ws);
+    SFM_LAUNCH(launch_gemv(c, 1, w->mod_w, w->mod_b, b.mod, B, 4 * D, d->adaln_dim, st));
+    if (fmt == SFM_W_FP8_E4M3) {
+        SFM_LAUNCH(launch_adaln_fp8(x_in, L, 0, L, b.mod, ms, b.hq, b.hs, B, D, d->eps, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+    } else {
+        SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, b.mod, ms, b.h, B, D, d->eps, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+    }
+    SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T, gh,
+                                   gw, H, d->eps, st));
+    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, st));
+    uint16_t* s = b.qkv;  // qkv is dead after the rotary step
+    if (fmt == SFM_W_FP8_E4M3) {
+        SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
+        SFM_LAUNCH(launch_adaln_fp8(x_out, L, 0, L, b.mod + 2 * D, ms, b.hq, b.hs, B, D, d->eps, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(launch_quant_rows(s, M, F, b.oq, b.os, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
+    } else {
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.o, nullptr, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
+        SFM_LAUNCH(launch_adaln_bf16(x_out, L, 0, L, b.mod + 2 * D, ms, b.h, B, D, d->eps, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.h, nullptr, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, s, nullptr, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
+    }
+    return SFM_OK;
+}
+
+struct StepWs {
+    float* e;
+    float* hdn;
+    float* c;
+    uint16_t* x;
+    float* sf;
+    uint16_t* hf;
+    void* block;
+    size_t bytes;
+};
+
+StepWs plan_model(const sfm_dims* d, int B, int T, int gh, int gw, void* base) {
+    const int64_t L = T + (int64_t)gh * gw, N = (int64_t)gh * gw, D = d->emb_dim, A = d->adaln_dim;
+    Carve c(base);
+    StepWs w{};
+    w.e = c.take<float>(B * A);
+    w.hdn = c.take<float>(B * A);
+    w.c = c.take<float>(B * A);
+    w.x = c.take<uint16_t>(B * L * D);
+    w.sf = c.take<float>(B * D);
+    w.hf = c.take<uint16_t>(B * N * D);
+    const size_t blk = plan_block(d, B, T, gh, gw, SFM_W_FP8_E4M3, nullptr).bytes;
+    w.block = c.take<char>(blk);
+    w.bytes = c.off + 256;
+    return w;
+}
+
+int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
+    if (!mw) return fail(SFM_E_INVALID_ARG, "model weights are NULL");
+    if (mw->num_layers < 0 || (mw->num_layers > 0 && !mw->blocks))
+        return fail(SFM_E_INVALID_ARG, "num_layers / blocks invalid");
+    for (int i = 0; i < mw->num_layers; ++i) {
+        int fmt = 0;
+        SFM_CHECK(check_block_weights(d, &mw->blocks[i], &fmt));
+        if (fmt != SFM_W_FP8_E4M3) return fail(SFM_E_INVALID_ARG, "layer %d: the velocity model takes FP8 blocks", i);
+    }
+    const void* ps[] = {mw->x_w, mw->x_b, mw->t_w1, mw->t_b1, mw->t_w2, mw->t_b2, mw->f_mod_w, mw->f_mod_b, mw->f_w, mw->f_b};
+    const char* names[] = {"x_w", "x_b", "t_w1", "t_b1", "t_w2", "t_b2", "f_mod_w", "f_mod_b", "f_w", "f_b"};
+    for (int i = 0; i < 10; ++i) SFM_CHECK(check_ptr(ps[i], names[i]));
+    return SFM_OK;
+}
+
+int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent, float t,
+              float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st) {
+    const sfm_dims* d = &ctx->dims;
+    const int N = gh * gw, L = T + N, D = d->emb_dim, A = d->adaln_dim, C = d->latent_ch;
+    StepWs w = plan_model(d, B, T, gh, gw, ws);
+    SFM_LAUNCH(launch_timestep_embed(t, w.e, B, A, st));
+    SFM_LAUNCH(launch_gemv(w.e, 0, mw->t_w1, mw->t_b1, w.hdn, B, A, A, st));
+    SFM_LAUNCH(launch_gemv(w.hdn, 1, mw->t_w2, mw->t_b2, w.c, B, A, A, st));
+    if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
+    SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
+    for (int i = 0; i < mw->num_layers; ++i)
+        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st));
+    SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
+    SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
+    SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
+                                   B * N, C, D, st));
+    return SFM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sfm_dims sfm_dims_ideogram4(void) {
+    sfm_dims d;
+    d.emb_dim = 4608;
+    d.num_heads = 18;
+    d.head_dim = 256;
+    d.intermediate = 12288;
+    d.adaln_dim = 512;
+    d.latent_ch = 128;
+    d.rope_dims = 128;
+    d.mrope_section[0] = 24;
+    d.mrope_section[1] = 20;
+    d.mrope_section[2] = 20;
+    d.max_text = 2048;
+    d.rope_theta = 5e6f;
+    d.eps = 1e-6f;
+    return d;
+}
+
+sfm_dims sfm_dims_tiny(void) {
+    sfm_dims d = sfm_dims_ideogram4();
+    d.emb_dim = 512;
+    d.num_heads = 2;
+    d.intermediate = 1536;
+    return d;
+}
+
+const char* sfm_status_string(int s) {
+    switch (s) {
+        case SFM_OK: return "ok";
+        case SFM_E_INVALID_ARG: return "invalid argument";
+        case SFM_E_SHAPE: return "unsupported shape";
+        case SFM_E_WORKSPACE: return "workspace too small";
+        case SFM_E_ARCH: return "device is not gfx950";
+        case SFM_E_ALIGN: return "pointer not 16-byte aligned";
+        case SFM_E_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* sfm_last_error(void) { return g_err.c_str(); }
+
+int sfm_check_shape(const sfm_dims* dims, int B, int T, int gh, int gw) {
+    SFM_CHECK(check_dims(dims));
+    return shape_check(dims, B, T, gh, gw);
+}
+
+int sfm_positions(int T, int gh, int gw, int32_t* pos) {
+    if (!pos) return fail(SFM_E_INVALID_ARG, "pos is NULL");
+    if (T < 0 || gh < 0 || gw < 0) return fail(SFM_E_SHAPE, "negative shape");
+    for (int i = 0; i < T; ++i) pos[3 * i] = pos[3 * i + 1] = pos[3 * i + 2] = i;
+    for (int r = 0; r < gh; ++r)
+        for (int c = 0; c < gw; ++c) {
+            int32_t* p = pos + 3 * (T + r * gw + c);
+            p[0] = T;
+            p[1] = T + r;
+            p[2] = T + c;
+        }
+    return SFM_OK;
+}
+
+int sfm_padded_len(int L) { return padded_len(L); }
+
+int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out) {
+    if (!out) return fail(SFM_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    SFM_CHECK(check_dims(dims));
+    int n = 0;
+    SFM_TRY_HIP(hipGetDeviceCount(&n));
+    if (device < 0 || device >= n) return fail(SFM_E_INVALID_ARG, "device %d of %d", device, n);
+    hipDeviceProp_t prop;
+    SFM_TRY_HIP(hipGetDeviceProperties(&prop, device));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SFM_E_ARCH, "device %d is %s, this library is built for gfx950", device, prop.gcnArchName);
+    int prev = 0;
+    SFM_TRY_HIP(hipGetDevice(&prev));
+    SFM_TRY_HIP(hipSetDevice(device));
+    sfm_context* ctx = new sfm_context();
+    ctx->dims = *dims;
+    ctx->device = device;
+    ctx->max_pos = dims->max_text + 128;
+    // MRoPE table: pair j rotates by pos * theta^(-j/64), computed in double and rounded to fp32
+    std::vector<float> cs((size_t)ctx->max_pos * 64), sn((size_t)ctx->max_pos * 64);
+    for (int p = 0; p < ctx->max_pos; ++p)
+        for (int j = 0; j < 64; ++j) {
+            const double inv_freq = pow((double)dims->rope_theta, -(double)j / 64.0);
+            const double a = (double)p * inv_freq;
+            cs[(size_t)p * 64 + j] = (float)cos(a);
+            sn[(size_t)p * 64 + j] = (float)sin(a);
+        }
+    build_nf4_codebook(ctx->nf4_code);
+    hipError_t e = hipMalloc((void**)&ctx->rope_cos, cs.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&ctx->rope_sin, sn.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(ctx->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(ctx->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice);
+    (void)hipSetDevice(prev);
+    if (e != hipSuccess) {
+        sfm_context_destroy(ctx);
+        return fail(SFM_E_DEVICE, "context tables: %s", hipGetErrorString(e));
+    }
+    *out = ctx;
+    return SFM_OK;
+}
+
+void sfm_context_destroy(sfm_context* ctx) {
+    if (!ctx) return;
+    if (ctx->rope_cos) (void)hipFree(ctx->rope_cos);
+    if (ctx->rope_sin) (void)hipFree(ctx->rope_sin);
+    delete ctx;
+}
+
+int sfm_modulation(const sfm_context* ctx, const uint16_t* w, const float* bias, const float* c, float* mod, int B,
+                   int n_out, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(check_ptr(w, "w"));
+    SFM_CHECK(check_ptr(c, "c"));
+    SFM_CHECK(check_ptr(mod, "mod"));
+    if (bias) SFM_CHECK(check_ptr(bias, "bias"));
+    if (B < 1 || B > 8 || n_out < 1) return fail(SFM_E_SHAPE, "B in [1, 8] and n_out >= 1 required");
+    SFM_LAUNCH(launch_gemv(c, 1, w, bias, mod, B, n_out, ctx->dims.adaln_dim, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+static int adaln_checks(const sfm_context* ctx, const uint16_t* x, const float* scale, int64_t stride, int B, int L) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(check_ptr(x, "x"));
+    SFM_CHECK(check_ptr(scale, "scale"));
+    if (B < 1 || L < 1) return fail(SFM_E_SHAPE, "B and L must be positive");
+    if (B > 1 && (stride < ctx->dims.emb_dim || stride % 4))
+        return fail(SFM_E_INVALID_ARG, "mod_batch_stride must be >= emb_dim and a multiple of 4");
+    return SFM_OK;
+}
+
+int sfm_adaln_norm_fp8(const sfm_context* ctx, const uint16_t* x, const float* scale, int64_t stride, uint8_t* hq,
+                       float* hs, int B, int L, void* stream) {
+    SFM_CHECK(adaln_checks(ctx, x, scale, stride, B, L));
+    SFM_CHECK(check_ptr(hq, "hq"));
+    if (!hs) return fail(SFM_E_INVALID_ARG, "hs is NULL");
+    SFM_LAUNCH(launch_adaln_fp8(x, L, 0, L, scale, stride, hq, hs, B, ctx->dims.emb_dim, ctx->dims.eps,
+                                (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_adaln_norm_bf16(const sfm_context* ctx, const uint16_t* x, const float* scale, int64_t stride, uint16_t* h,
+                        int B, int L, void* stream) {
+    SFM_CHECK(adaln_checks(ctx, x, scale, stride, B, L));
+    SFM_CHECK(check_ptr(h, "h"));
+    SFM_LAUNCH(launch_adaln_bf16(x, L, 0, L, scale, stride, h, B, ctx->dims.emb_dim, ctx->dims.eps,
+                                 (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_quant_rows_fp8(const uint16_t* a, int rows, int cols, uint8_t* q, float* s, void* stream) {
+    SFM_CHECK(check_ptr(a, "a"));
+    SFM_CHECK(check_ptr(q, "q"));
+    if (!s) return fail(SFM_E_INVALID_ARG, "s is NULL");
+    if (rows < 0 || cols < 8 || cols % 8 || cols > 16384)
+        return fail(SFM_E_SHAPE, "cols must be a multiple of 8 in [8, 16384]");
+    SFM_LAUNCH(launch_quant_rows(a, rows, cols, q, s, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_scale, const sfm_qweight* w,
+               uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int L,
+               void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    if (epi < SFM_EPI_STORE || epi > SFM_EPI_SWIGLU) return fail(SFM_E_INVALID_ARG, "unknown epilogue %d", epi);
+    if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
+    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format");
+    SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
+    if (w->n < 256 || w->n % 256 || w->k < 128 || w->k % 128)
+        return fail(SFM_E_SHAPE, "weight [%d][%d]: need n %% 256 == 0 and k %% 128 == 0", w->n, w->k);
+    SFM_CHECK(check_ptr(a, "a"));
+    SFM_CHECK(check_ptr(out, "out"));
+    if (w->fmt == SFM_W_FP8_E4M3 && !a_scale) return fail(SFM_E_INVALID_ARG, "a_scale is NULL");
+    if (M < 0 || L < 1) return fail(SFM_E_SHAPE, "M >= 0 and L >= 1 required");
+    if (epi == SFM_EPI_RESID_GATE) {
+        SFM_CHECK(check_ptr(resid, "resid"));
+        if (!gate) return fail(SFM_E_INVALID_ARG, "gate is NULL");
+        if (M > L && gate_stride < w->n) return fail(SFM_E_INVALID_ARG, "gate_batch_stride < n");
+    }
+    SFM_LAUNCH(gemm(ctx, epi, a, a_scale, w, out, resid, gate, gate_stride, M, L, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
+                     uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh, int gw, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    const void* ps[] = {qkv, q_norm, k_norm, q, k, vt};
+    const char* ns[] = {"qkv", "q_norm", "k_norm", "q", "k", "vt"};
+    for (int i = 0; i < 6; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
+    SFM_LAUNCH(launch_qk_norm_rope(qkv, q_norm, k_norm, ctx->rope_cos, ctx->rope_sin, q, k, vt, B, T, gh, gw,
+                                   ctx->dims.num_heads, ctx->dims.eps, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_attention(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o,
+                  int B, int L, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(check_ptr(q, "q"));
+    SFM_CHECK(check_ptr(k, "k"));
+    SFM_CHECK(check_ptr(vt, "vt"));
+    SFM_CHECK(check_ptr(o, "o"));
+    if (B < 1 || L < 1 || L > ctx->dims.max_text + 128 * 128) return fail(SFM_E_SHAPE, "B / L out of range");
+    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_euler_cfg(const float* z, const float* v_c, const float* v_u, float* z_out, float* v_out, int64_t n,
+                  float guidance, float dt, void* stream) {
+    SFM_CHECK(check_ptr(z, "z"));
+    SFM_CHECK(check_ptr(v_c, "v_c"));
+    SFM_CHECK(check_ptr(v_u, "v_u"));
+    SFM_CHECK(check_ptr(z_out, "z_out"));
+    if (v_out) SFM_CHECK(check_ptr(v_out, "v_out"));
+    if (n < 0) return fail(SFM_E_SHAPE, "n < 0");
+    if (!isfinite(guidance) || !isfinite(dt)) return fail(SFM_E_INVALID_ARG, "guidance / dt not finite");
+    SFM_LAUNCH(launch_euler_cfg(z, v_c, v_u, z_out, v_out, n, guidance, dt, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_dequant(const sfm_context* ctx, const sfm_qweight* w, void* out, int out_dtype, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
+    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format");
+    SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
+    SFM_CHECK(check_ptr(out, "out"));
+    if (out_dtype != 0 && out_dtype != 1) return fail(SFM_E_INVALID_ARG, "out_dtype must be 0 (fp32) or 1 (bf16)");
+    if (w->n < 1 || w->k < 64 || w->k % 64) return fail(SFM_E_SHAPE, "k must be a positive multiple of 64");
+    const hipStream_t st = (hipStream_t)stream;
+    if (w->fmt == SFM_W_FP8_E4M3) {
+        SFM_LAUNCH(launch_dequant_fp8((const uint8_t*)w->q, w->scale, out, out_dtype, w->n, w->k, st));
+    } else {
+        Nf4Code code;
+        memcpy(code.v, ctx->nf4_code, sizeof code.v);
+        SFM_LAUNCH(launch_dequant_nf4((const uint8_t*)w->q, w->scale, code, out, out_dtype, w->n, w->k, st));
+    }
+    return SFM_OK;
+}
+
+size_t sfm_block_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw, int wfmt) {
+    if (!ctx) return 0;
+    return plan_block(&ctx->dims, B, T, gh, gw, wfmt, nullptr).bytes;
+}
+
+int sfm_block_forward(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in, uint16_t* x_out,
+                      const float* c, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    int fmt = 0;
+    SFM_CHECK(check_block_weights(&ctx->dims, w, &fmt));
+    SFM_CHECK(check_ptr(x_in, "x_in"));
+    SFM_CHECK(check_ptr(x_out, "x_out"));
+    SFM_CHECK(check_ptr(c, "c"));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    const size_t need = plan_block(&ctx->dims, B, T, gh, gw, fmt, nullptr).bytes;
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return run_block(ctx, w, fmt, x_in, x_out, c, B, T, gh, gw, ws, (hipStream_t)stream);
+}
+
+size_t sfm_step_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw) {
+    if (!ctx) return 0;
+    const size_t n = (size_t)B * gh * gw * ctx->dims.latent_ch;
+    Carve c(nullptr);
+    c.take<float>(n);
+    c.take<float>(n);
+    c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    return c.off + 256;
+}
+
+int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent,
+                       float t, float* v_out, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    SFM_CHECK(check_model_weights(&ctx->dims, mw));
+    if (T > 0) SFM_CHECK(check_ptr(text, "text"));
+    SFM_CHECK(check_ptr(latent, "latent"));
+    SFM_CHECK(check_ptr(v_out, "v_out"));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    if (!isfinite(t)) return fail(SFM_E_INVALID_ARG, "t not finite");
+    const size_t need = plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes;
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return run_model(ctx, mw, text, latent, t, v_out, B, T, gh, gw, ws, (hipStream_t)stream);
+}
+
+int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                 const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B, int T,
+                 int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    SFM_CHECK(check_model_weights(&ctx->dims, cond));
+    SFM_CHECK(check_model_weights(&ctx->dims, uncond));
+    if (T > 0) SFM_CHECK(check_ptr(text, "text"));
+    SFM_CHECK(check_ptr(z, "z"));
+    SFM_CHECK(check_ptr(z_out, "z_out"));
+    if (v_c_out) SFM_CHECK(check_ptr(v_c_out, "v_c_out"));
+    if (v_u_out) SFM_CHECK(check_ptr(v_u_out, "v_u_out"));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    if (!isfinite(t) || !isfinite(dt) || !isfinite(guidance))
+        return fail(SFM_E_INVALID_ARG, "t / dt / guidance not finite");
+    const size_t need = sfm_step_workspace_bytes(ctx, B, T, gh, gw);
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    const size_t n = (size_t)B * gh * gw * ctx->dims.latent_ch;
+    Carve c(ws);
+    float* vc = c.take<float>(n);
+    float* vu = c.take<float>(n);
+    void* mws = c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    if (v_c_out) vc = v_c_out;
+    if (v_u_out) vu = v_u_out;
+    const hipStream_t st = (hipStream_t)stream;
+    SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws, st));
+    SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws, st));
+    SFM_LAUNCH(launch_euler_cfg(z, vc, vu, z_out, nullptr, (int64_t)n, guidance, dt, st));
+    return SFM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// Internal declarations of the gfx950 DiT library: the context, device helpers
+// shared by the kernels, and the host launchers each kernel file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sfm.h"
+
+struct sfm_context {
+    sfm_dims dims;
+    int device;
+    int max_pos;          // rows of the rotary tables: max_text + 128 image positions
+    float* rope_cos;      // device [max_pos][64] fp32
+    float* rope_sin;      // device [max_pos][64] fp32
+    float nf4_code[16];   // NF4 codebook (fp32), passed to kernels by value
+};
+
+namespace sfm {
+
+struct Nf4Code {
+    float v[16];
+};
+
+// ------------------------------------------------------------------ device helpers
+#if defined(__HIPCC__)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Two fp32 -> two OCP E4M3 codes in the low (word 0) or high (word 1) half of
+// `old`, hardware round-to-nearest-even.  Callers clamp to +-448 first.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Reduction over a workgroup of NW waves through `red` (NW floats of LDS).
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += red[i];
+    return t;
+}
+
+template <int NW>
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float t = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t = fmaxf(t, red[i]);
+    return t;
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+#endif  // __HIPCC__
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+inline int padded_len(int L) { return (int)round_up(L, 128); }
+
+// ------------------------------------------------------------------ launchers
+// All launchers enqueue on `st` and return hipError_t of the launch.
+
+// k_norm.hip
+hipError_t launch_gemv(const float* in, int act_silu, const uint16_t* w, const float* bias, float* out, int B,
+                       int n_out, int k, hipStream_t st);
+hipError_t launch_adaln_fp8(const uint16_t* x, int64_t rows_per_batch_in, int64_t row_off, int rows_per_batch,
+                            const float* scale, int64_t scale_stride, uint8_t* hq, float* hs, int B, int D, float eps,
+                            hipStream_t st);
+hipError_t launch_adaln_bf16(const uint16_t* x, int64_t rows_per_batch_in, int64_t row_off, int rows_per_batch,
+                             const float* scale, int64_t scale_stride, uint16_t* h, int B, int D, float eps,
+                             hipStream_t st);
+hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_timestep_embed(float t, float* e, int B, int dim, hipStream_t st);
+
+// k_gemm_fp8.hip
+hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
+                           uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
+                           int K, int L, hipStream_t st);
+
+// k_gemm_nf4.hip
+hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,
+                           uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
+                           int K, int L, hipStream_t st);
+
+// k_rope.hip
+hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const uint16_t* kn, const float* cos_t,
+                               const float* sin_t, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh,
+                               int gw, int H, float eps, hipStream_t st);
+
+// k_attn.hip
+hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o, int B, int L,
+                            int H, hipStream_t st);
+
+// k_misc.hip
+hipError_t launch_euler_cfg(const float* z, const float* vc, const float* vu, float* zo, float* vo, int64_t n,
+                            float g, float dt, hipStream_t st);
+hipError_t launch_dequant_fp8(const uint8_t* q, const float* s, void* out, int out_bf16, int n, int k,
+                              hipStream_t st);
+hipError_t launch_dequant_nf4(const uint8_t* q, const float* absmax, const Nf4Code& code, void* out, int out_bf16,
+                              int n, int k, hipStream_t st);
+// out[m][n] = sum_k a[m][k] w[n][k] + bias[n]; a fp32 or bf16, w bf16, out bf16 or fp32.
+// Row m of `a` is read at a_row(m) = (m / a_rpb) * a_bstride + a_off + m % a_rpb, same for out.
+hipError_t launch_small_linear(const void* a, int a_bf16, int64_t a_rpb, int64_t a_bstride, int64_t a_off,
+                               const uint16_t* w, const float* bias, void* out, int out_bf16, int64_t o_rpb,
+                               int64_t o_bstride, int64_t o_off, int M, int N, int K, hipStream_t st);
+hipError_t launch_copy_rows(const uint16_t* src, int64_t src_rpb, uint16_t* dst, int64_t dst_rpb, int B,
+                            int rows, int cols, hipStream_t st);
+
+}  // namespace sfm

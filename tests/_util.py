@@ -1,0 +1,58 @@
+"""Glue between the seeded inputs, the oracle and the GPU binding (tests only)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import dit as O
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 values of a (CPU or device) float / bf16 tensor."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def npu8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").numpy().astype(np.uint8)
+
+
+def oracle_weight(fmt, pair):
+    q, s = pair
+    if fmt == "fp8":
+        return O.Fp8Weight(npu8(q), s.detach().cpu().numpy().astype(np.float32))
+    n, k2 = q.shape
+    return O.Nf4Weight(npu8(q), s.detach().cpu().numpy().astype(np.float32), n, 2 * k2)
+
+
+def oracle_block(p) -> O.BlockWeights:
+    return O.BlockWeights(oracle_weight(p.fmt, p.qkv), oracle_weight(p.fmt, p.o), oracle_weight(p.fmt, p.gate_up),
+                          oracle_weight(p.fmt, p.down), np64(p.q_norm), np64(p.k_norm), np64(p.mod_w),
+                          p.mod_b.detach().cpu().numpy().astype(np.float32))
+
+
+def oracle_model(p) -> O.ModelWeights:
+    f32 = lambda t: t.detach().cpu().numpy().astype(np.float32)
+    return O.ModelWeights([oracle_block(b) for b in p.blocks], np64(p.x_w), f32(p.x_b), np64(p.t_w1), f32(p.t_b1),
+                          np64(p.t_w2), f32(p.t_b2), np64(p.f_mod_w), f32(p.f_mod_b), np64(p.f_w), f32(p.f_b))
+
+
+def to_device(obj, device="cuda"):
+    """Copy every tensor field of a synth dataclass (recursively) to the device."""
+    import dataclasses
+    if isinstance(obj, torch.Tensor):
+        return obj.to(device)
+    if isinstance(obj, tuple):
+        return tuple(to_device(x, device) for x in obj)
+    if isinstance(obj, list):
+        return [to_device(x, device) for x in obj]
+    if dataclasses.is_dataclass(obj):
+        return dataclasses.replace(obj, **{f.name: to_device(getattr(obj, f.name), device)
+                                           for f in dataclasses.fields(obj)})
+    return obj
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
