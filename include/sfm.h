@@ -178,7 +178,7 @@ typedef enum sfm_epilogue {
  * NF4 weights: a = bf16 [M][k], a_scale unused; y = a * bf16(w)^T on bf16
  * matrix cores, the NF4 decode fused into the weight-operand load.
  * gate: fp32, row b of the batch at gate + b*gate_batch_stride (n values);
- * L gives the batch of a row (b = m / L).  k % 128 == 0, n % 256 == 0. */
+ * L gives the batch of a row (b = m / L).  k % 256 == 0, n % 256 == 0. */
 int sfm_linear(const sfm_context* ctx, int epilogue, const void* a, const float* a_scale, const sfm_qweight* w,
                uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_batch_stride, int M, int L,
                void* stream);
@@ -193,8 +193,10 @@ int sfm_padded_len(int L);
  * by pos[axis(j)] * theta^(-j/64) with axis t for j < 24, h for j < 44, w
  * otherwise; dims 128..255 pass through; result rounded to bf16.
  * Outputs (Lp = sfm_padded_len(L)): q, k bf16 [B][H][Lp][256]; vt fp16
- * [B][H][256][Lp] (v transposed, token-contiguous; the bf16 values of v are
- * exact in fp16, values beyond +-65504 saturate).  Padding rows / columns are
+ * [B][H][256][Lp] (v transposed; the bf16 values of v are exact in fp16 down
+ * to 2^-17, values beyond +-65504 saturate).  Inside every aligned group of 32
+ * tokens vt stores the tokens in the order 4g..4g+3, 16+4g..16+4g+3 for
+ * g = 0..3 (the attention kernel's operand order).  Padding rows / columns are
  * written as zeros. */
 int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                      uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh, int gw, void* stream);

@@ -68,13 +68,25 @@ __device__ __forceinline__ void gemm_epilogue(const v4f (&acc)[FM][FN], int m0w,
     }
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs; renumber so that
-// each XCD gets a contiguous range of tiles and neighbouring tiles share its L2.
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8); renumber so that each XCD gets one contiguous range of ids and
+// the tiles it works on at the same time share its L2.
 __device__ __forceinline__ int xcd_tile_id() {
-    int bid = blockIdx.x;
-    const int nwg = gridDim.x;
-    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    return bid;
+    const int b = blockIdx.x, n = gridDim.x;
+    const int q = n >> 3, r = n & 7, x = b & 7;
+    return x * q + min(x, r) + (b >> 3);
+}
+
+// Tile (tm, tn) of linear id t in a grouped raster: ids walk GM tile-rows down
+// before moving one tile-column right, so a run of 32 ids touches GM A
+// row-blocks and 32 / GM weight column-blocks.
+__device__ __forceinline__ void grouped_tile(int t, int ntm, int ntn, int GM, int& tm, int& tn) {
+    const int group = t / (GM * ntn);
+    const int first = group * GM;
+    const int gm = min(ntm - first, GM);
+    const int r = t - group * GM * ntn;
+    tm = first + r % gm;
+    tn = r / gm;
 }
 
 }  // namespace sfm

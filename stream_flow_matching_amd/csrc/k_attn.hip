@@ -4,22 +4,31 @@
 // over the whole [text | image] sequence.  o = softmax(q k^T / 16) v per head.
 //
 // Layout: a workgroup owns 128 queries of one (batch, head); each of its four
-// waves owns 32 queries whose q fragments stay in registers.  Key tiles of 64
-// keys stream through LDS (K as [key][d], V^T as [d][key]).
+// waves owns 32 queries whose q fragments stay in registers.  Tiles of 64 keys
+// stream global -> LDS with buffer_load ... lds (no staging registers): K as
+// [key][d] and V^T as [d][key], two stages of 64 KiB, one barrier per tile.
 // Per tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K
 // rows, B = Q rows), so every lane holds the scores of ONE query column
 // (lane & 15) for keys 4*(lane>>4)+r: the softmax max is a reduction over the
 // lane's values and the 4 lanes sharing the column; the running sum stays a
 // per-lane partial until the end.  P^T then feeds O^T += V^T P^T directly from
-// registers as the B operand (keys k-sliced identically in the V^T operand),
-// and O^T's query column is again lane-local, so rescaling is lane-local too.
+// registers as the B operand, and O^T's query column is again lane-local, so
+// rescaling is lane-local too.  The running max is only moved when a tile
+// raises it by more than 2^8 (scores then stay below 2^8 relative to the kept
+// max), which skips most rescales of the 128-register accumulator.
+//
 // The P V product runs in fp16 (P and V^T in fp16, fp32 accumulation): fp16
 // keeps 3 more mantissa bits of P than bf16, and V's bf16 values are exact in
 // fp16.  P in bf16 perturbs o by about 1e-3 relative, which the per-token FP8
 // quantisation of o downstream turns into percent-level changes of the block.
-// The running max is only moved when a tile raises it by more than 2^8
-// (scores then stay below 2^8 relative to the kept max), which skips most
-// rescales of the 128-register accumulator.
+//
+// LDS rows are XOR-swizzled in 16-byte chunks, applied through the source
+// addresses of the direct loads: K rows (512 bytes) by row & 15, V^T rows (128
+// bytes, two per 256-byte bank line) by (row >> 1) & 7, so the 16 rows one
+// operand read touches land in 16 distinct 16-byte bank slots.  V^T's key
+// order inside every group of 32 keys is [4g..4g+3, 16+4g..16+4g+3] for
+// g = 0..3 (written that way by the rotary kernel), so a lane's eight P^T keys
+// are one 16-byte chunk.
 #include "sfm_internal.h"
 
 namespace sfm {
@@ -31,27 +40,42 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQB = 128;  // queries per workgroup
-constexpr int kKB = 64;   // keys per tile
+#define SFM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kQB = 128;              // queries per workgroup
+constexpr int kKB = 64;               // keys per tile
 constexpr int kD = 256;
-// LDS rows are padded so that the 8 (K, 16-byte reads) or 16 (V^T, 8-byte
-// reads) rows read together start in different banks, and every fragment
-// address is a per-lane base plus a compile-time offset.
-constexpr int kKRow = kD * 2 + 16;   // K tile row (one key): 528 B
-constexpr int kVRow = kKB * 2 + 8;   // V^T tile row (one d): 136 B
-constexpr int kKBytes = kKB * kKRow;
-constexpr int kVBytes = kD * kVRow;
+constexpr int kKTile = kKB * kD * 2;  // 32 KiB
+constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ int k_off(int key, int chunk16) { return key * kKRow + chunk16 * 16; }
-__device__ __forceinline__ int v_off(int d, int chunk8) { return d * kVRow + chunk8 * 8; }
+struct Loader {
+    __amdgpu_buffer_rsrc_t rk, rv;
+    uint32_t kvoff[2];      // per-lane byte offsets inside a K tile (even / odd wave-load)
+    uint32_t vvoff;         // per-lane byte offset inside a V^T tile
+    uint32_t lds0;          // this wave's first 1 KiB destination inside a tile
+    int Lp2;                // bytes per V^T row
+
+    // 16 wave-level loads: 8 for the K tile (2 rows each), 8 for the V^T tile (8 rows each)
+    __device__ __forceinline__ void issue(uint8_t* stage, int key0) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, SFM_LDS(stage + lds0 + i * 4096), 16, kvoff[i & 1],
+                                                     (uint32_t)(key0 + 8 * i) * 512u, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, SFM_LDS(stage + kKTile + lds0 + i * 4096), 16, vvoff,
+                                                     (uint32_t)(32 * i * Lp2 + key0 * 2), 0, 0);
+    }
+};
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ o, int L, int Lp, int H, int nqb) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* const ktile = smem;               // [64 keys][256 d]
-    uint8_t* const vtile = smem + kKBytes;  // [256 d][64 keys]
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kKTile];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kKTile];
 
     // XCD-aware order: each XCD gets a contiguous run of (head, query-block) pairs
     int bid = blockIdx.x;
@@ -64,9 +88,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const uint16_t* Qh = q + (int64_t)bh * Lp * kD;
-    const uint16_t* Kh = k + (int64_t)bh * Lp * kD;
-    const uint16_t* Vh = vt + (int64_t)bh * kD * Lp;
     const int q0 = qb * kQB + wave * 32;
+
+    Loader ld;
+    ld.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (int64_t)bh * Lp * kD), 0, Lp * kD * 2, kRsrcWord3);
+    ld.rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (int64_t)bh * kD * Lp), 0, kD * Lp * 2, kRsrcWord3);
+    ld.Lp2 = Lp * 2;
+    ld.lds0 = (uint32_t)wave * 1024;
+    {
+        // K tile: 1 KiB block (wave + 4i) holds rows r = 2(wave + 4i) + (lane >> 5) (relative to the
+        // tile), physical chunk lane & 31 = logical chunk ^ (r & 15); r & 15 depends on i only through
+        // 8 (i & 1)
+        for (int par = 0; par < 2; ++par) {
+            const int r = 2 * wave + 8 * par + (lane >> 5);
+            ld.kvoff[par] = (uint32_t)((r - 8 * par) * 512 + (((lane & 31) ^ (r & 15)) * 16));
+        }
+        // V^T tile: 1 KiB block (wave + 4i) holds rows 8(wave + 4i) + (lane >> 3), physical chunk lane & 7
+        // = logical chunk ^ ((row >> 1) & 7) = logical ^ ((4 (wave & 1) + (lane >> 4)) & 7)
+        const int vrow = 8 * wave + (lane >> 3);
+        ld.vvoff = (uint32_t)(vrow * Lp * 2 + (((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) * 16));
+    }
 
     // q fragments (B operand of S^T): rows q0 + qt*16 + lr, dims ks*32 + 8*lg .. +8
     bf16x8 qf[2][8];
@@ -77,39 +118,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             qf[qt][ks] = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4*>(Qh + (int64_t)(q0 + qt * 16 + lr) * kD + ks * 32 + 8 * lg));
 
-    // tile staging: K tile = 64 rows x 32 chunks of 16 B (8 per thread);
-    // V^T tile = 256 rows x 8 chunks of 16 B (8 per thread)
-    u32x4 rst[8];
-    auto gload_k = [&](int key0) {
+    // fragment read offsets.  K rows t4*16 + lr: chunk (ks*4 + lg) ^ lr = 4 (ks ^ (lr >> 2)) + (lg ^ (lr & 3)),
+    // so ks = 4 u + m reads at kb[m] + u * 256.  V^T rows dt*16 + lr: chunk (h2*4 + lg) ^ ((lr >> 1) & 7).
+    int kb[4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = tid + c * 256;
-            rst[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)(key0 + (i >> 5)) * kD + (i & 31) * 8);
-        }
-    };
-    auto lstore_k = [&]() {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = tid + c * 256;
-            *reinterpret_cast<u32x4*>(ktile + k_off(i >> 5, i & 31)) = rst[c];
-        }
-    };
-    auto gload_v = [&](int key0) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = tid + c * 256;
-            rst[c] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)(i >> 3) * Lp + key0 + (i & 7) * 8);
-        }
-    };
-    auto lstore_v = [&]() {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int i = tid + c * 256;
-            const int d = i >> 3, c16 = i & 7;
-            *reinterpret_cast<u32x2*>(vtile + v_off(d, 2 * c16)) = u32x2{rst[c].x, rst[c].y};
-            *reinterpret_cast<u32x2*>(vtile + v_off(d, 2 * c16 + 1)) = u32x2{rst[c].z, rst[c].w};
-        }
-    };
+    for (int m = 0; m < 4; ++m) kb[m] = lr * 512 + ((lg ^ (lr & 3)) << 4) + ((m ^ (lr >> 2)) << 6);
+    const int x = (lr >> 1) & 7;
+    const int csw = (lg ^ (x & 3)) << 4;
+    const int vb0 = lr * 128 + csw + ((x >> 2) << 6);        // keys 0..31 of the tile
+    const int vb1 = lr * 128 + csw + ((1 ^ (x >> 2)) << 6);  // keys 32..63
 
     v4f oacc[2][16];
 #pragma unroll
@@ -120,37 +137,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float lsum[2] = {0.f, 0.f};
     const float cs = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
 
-    const int nkt = (L + kKB - 1) / kKB;
-    // Pipeline, one K buffer and one V^T buffer in LDS:
-    //   S phase reads K_i while K_{i+1} is fetched into registers; barrier A;
-    //   K_{i+1} -> LDS; PV phase reads V_i while V_{i+1} is fetched; barrier B;
-    //   V_{i+1} -> LDS (made visible by the next barrier A).
-    gload_k(0);
-    lstore_k();
-    gload_v(0);
-    lstore_v();
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int key0 = kt * kKB;
-        const bool more = kt + 1 < nkt;
-        if (more) gload_k(key0 + kKB);
-        const uint8_t* kl = ktile;
-        const uint8_t* vl = vtile;
-
+    auto compute = [&](const uint8_t* stg, int key0) {
+        const uint8_t* kl = stg;
+        const uint8_t* vl = stg + kKTile;
         // S^T tile: s[qt][t4][r] = score(key = t4*16 + 4*lg + r, query = qt*16 + lr)
         v4f s[2][4];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) s[qt][t4] = v4f{0.f, 0.f, 0.f, 0.f};
-        // K fragments double-buffered in registers, one d-slice (ks) ahead;
-        // the scheduling barriers keep the compiler from hoisting all 32 loads.
         bf16x8 kf[2][4];
         auto load_kf = [&](int slot, int ks) {
+            const int base = kb[ks & 3] + (ks >> 2) * 256;
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
-                kf[slot][t4] =
-                    __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + k_off(t4 * 16 + lr, ks * 4 + lg)));
+                kf[slot][t4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + base + t4 * 8192));
         };
         load_kf(0, 0);
 #pragma unroll
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
-                    s[qt][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
+                    s[qt][t4] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (key0 + kKB > L) {  // ragged last tile: mask keys >= L
@@ -178,11 +180,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         f16x8 pf[2][2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            float mx = -INFINITY;
+            float mx = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
 #pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qt][t4][r]);
+            for (int t4 = 1; t4 < 4; ++t4)
+                mx = fmaxf(mx, fmaxf(fmaxf(s[qt][t4][0], s[qt][t4][1]), fmaxf(s[qt][t4][2], s[qt][t4][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float mnew = fmaxf(mrun[qt], mx * cs);
@@ -197,35 +198,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             float ls = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                f16x8 ph;
+                // v_exp_f32 directly: results below 2^-126 flush to zero, which a
+                // softmax weight relative to a max of at least 1 can ignore
+                float p[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float p = exp2f(s[qt][2 * h2 + (e >> 2)][e & 3] * cs - mref);
-                    ph[e] = (_Float16)p;
-                    ls += (float)ph[e];
+                    p[e] = __builtin_amdgcn_exp2f(s[qt][2 * h2 + (e >> 2)][e & 3] * cs - mref);
+                    ls += p[e];
+                }
+                f16x8 ph;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const f16x2 hp = __builtin_convertvector(f32x2{p[e], p[e + 1]}, f16x2);
+                    ph[e] = hp[0];
+                    ph[e + 1] = hp[1];
                 }
                 pf[qt][h2] = ph;
             }
             lsum[qt] += ls;
         }
 
-        __syncthreads();  // A: every wave is done with K_i (and V_i is visible)
-        if (more) {
-            lstore_k();
-            gload_v(key0 + kKB);
-        }
-
-        // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]
-        // V^T fragments: 32 (h2, dt) groups, loaded four groups ahead
+        // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments four d-tiles ahead
         f16x8 vf[2][4];
-        auto load_vf = [&](int slot, int g) {  // groups 4g .. 4g+3: h2 = g / 4, dt = 4 (g % 4) + u
+        auto load_vf = [&](int slot, int g) {  // g = 0..7: h2 = g >> 2, d-tiles 4 (g & 3) .. +3
+            const int base = (g >> 2) ? vb1 : vb0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int h2 = g >> 2, d = (4 * (g & 3) + u) * 16 + lr;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vl + v_off(d, h2 * 8 + lg));
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vl + v_off(d, h2 * 8 + 4 + lg));
-                vf[slot][u] = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-            }
+            for (int u = 0; u < 4; ++u)
+                vf[slot][u] =
+                    __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vl + base + (4 * (g & 3) + u) * 2048));
         };
         load_vf(0, 0);
 #pragma unroll
@@ -237,12 +237,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 const int dt = 4 * (g & 3) + u;
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
-                    oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
+                    oacc[qt][dt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();  // B: every wave is done with V_i (and K_{i+1} is visible)
-        if (more) lstore_v();
+    };
+
+    // Two LDS stages: tile t lives in stage t & 1; the loads of tile t + 1 run
+    // during the compute of tile t; one barrier per tile.
+    const int nkt = (L + kKB - 1) / kKB;
+    ld.issue(st0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; kt += 2) {
+        if (kt + 1 < nkt) ld.issue(st1, (kt + 1) * kKB);
+        compute(st0, kt * kKB);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 >= nkt) break;
+        if (kt + 2 < nkt) ld.issue(st0, (kt + 2) * kKB);
+        compute(st1, (kt + 1) * kKB);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     // normalise and write o[b*L + query][h*256 + d]
@@ -275,13 +292,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     if (L == 0) return hipSuccess;
     const int Lp = padded_len(L);
     const int nqb = Lp / kQB;
-    const size_t shm = (size_t)kKBytes + kVBytes;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(256), shm, st, q, k, vt, o, L, Lp, H, nqb);
+    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(256), 0, st, q, k, vt, o, L, Lp, H, nqb);
     return hipGetLastError();
 }
 

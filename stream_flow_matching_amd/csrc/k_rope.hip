@@ -14,7 +14,9 @@
 // 128+2t+1; the rotation partner of dims 2t, 2t+1 lives in lane t ^ 32), and
 // the v slice is transposed through LDS into vt[b][h][d][token] as fp16 (every
 // bf16 value with |v| <= 65504 is exact in fp16; larger ones saturate), the
-// operand format of the attention kernel's P V product.
+// operand format of the attention kernel's P V product.  Inside every group of
+// 32 tokens the stored order is [4g..4g+3, 16+4g..16+4g+3] for g = 0..3: the
+// eight keys one lane of the attention kernel needs are then contiguous.
 #include "sfm_internal.h"
 
 namespace sfm {
@@ -110,13 +112,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
         }
     }
     __syncthreads();
-    // write vt[b][h][d][l0 .. l0+63]: thread writes 8 tokens (16 bytes) of one d row
+    // write vt[b][h][d][l0 .. l0+63]: thread writes stored slots 8c .. 8c+7 (16 bytes) of one d row;
+    // inside each group of 32 tokens, slot 8g + e holds token 4g + e (e < 4) or 16 + 4g + (e - 4)
     for (int i = threadIdx.x; i < 256 * (kTok / 8); i += 256) {
         const int d = i >> 3, c = i & 7;
+        const int t0 = 32 * (c >> 2) + 4 * (c & 3);
         uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[e] = (uint32_t)vs[d][c * 8 + 2 * e] | ((uint32_t)vs[d][c * 8 + 2 * e + 1] << 16);
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + (e >= 2 ? 16 : 0) + 2 * (e & 1);
+            w[e] = (uint32_t)vs[d][t] | ((uint32_t)vs[d][t + 1] << 16);
+        }
         uint16_t* dst = vt + (((int64_t)b * H + h) * 256 + d) * Lp + l0 + c * 8;
         *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
     }

@@ -476,8 +476,8 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
     if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
     if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format");
     SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
-    if (w->n < 256 || w->n % 256 || w->k < 128 || w->k % 128)
-        return fail(SFM_E_SHAPE, "weight [%d][%d]: need n %% 256 == 0 and k %% 128 == 0", w->n, w->k);
+    if (w->n < 256 || w->n % 256 || w->k < 256 || w->k % 256)
+        return fail(SFM_E_SHAPE, "weight [%d][%d]: need n %% 256 == 0 and k %% 256 == 0", w->n, w->k);
     SFM_CHECK(check_ptr(a, "a"));
     SFM_CHECK(check_ptr(out, "out"));
     if (w->fmt == SFM_W_FP8_E4M3 && !a_scale) return fail(SFM_E_INVALID_ARG, "a_scale is NULL");

@@ -56,3 +56,14 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def vt_order(n):
+    """Token stored at each position of the attention kernel's V^T rows: inside
+    every group of 32, positions 8g .. 8g+7 hold tokens 4g..4g+3, 16+4g..16+4g+3."""
+    idx = np.empty(n, np.int64)
+    for j in range(0, n, 32):
+        for g in range(4):
+            for e in range(8):
+                idx[j + 8 * g + e] = j + 4 * g + (e if e < 4 else 12 + e)
+    return idx

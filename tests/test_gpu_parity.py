@@ -21,7 +21,7 @@ import torch
 from oracle import dit as O
 from oracle import numerics as N
 from stream_flow_matching_amd import synth
-from tests._util import np64, npu8, oracle_block, oracle_model, rel_l2, to_device
+from tests._util import np64, npu8, oracle_block, oracle_model, rel_l2, to_device, vt_order
 
 pytestmark = pytest.mark.gpu
 
@@ -284,8 +284,11 @@ def test_qk_norm_rope(sfm, ctx_tiny, ctx_full, dims, B, T, gh, gw):
         assert rel_l2(gq, rq) < 2e-3 and rel_l2(gk, rk) < 2e-3
         # v is carried in fp16: the bf16 values convert exactly except below 2**-17 (fp16 subnormals)
         want_v = torch.from_numpy(x[b, rows, 2]).to(torch.bfloat16).to(torch.float16).double().numpy()
-        assert np.array_equal(np64(vt[b][:, :, rows]).transpose(2, 0, 1), want_v)
-    assert torch.all(q[:, :, L:] == 0) and torch.all(k[:, :, L:] == 0) and torch.all(vt[:, :, :, L:] == 0)
+        inv = np.argsort(vt_order(Lp))          # stored position of each token
+        assert np.array_equal(np64(vt[b][:, :, inv[rows]]).transpose(2, 0, 1), want_v)
+    pad_tokens = torch.from_numpy(np.argsort(vt_order(Lp))[L:])
+    assert torch.all(q[:, :, L:] == 0) and torch.all(k[:, :, L:] == 0)
+    assert torch.all(vt[:, :, :, pad_tokens.to(DEV)] == 0)
 
 
 # --------------------------------------------------------------------------- a5 attention
@@ -303,7 +306,7 @@ def test_attention(sfm, ctx_tiny, ctx_full, B, L, H):
     k[:, :, :L] = synth.bf16_normal((B, H, L, 256), ("ak", B, L, H), 1.0)
     vt[:, :, :, :L] = synth.bf16_normal((B, H, 256, L), ("av", B, L, H), 1.0).to(torch.float16)
     o = torch.empty(B * L, H * 256, dtype=torch.bfloat16, device=DEV)
-    sfm.sfm_attention(ctx, q.to(DEV), k.to(DEV), vt.to(DEV), o, B, L)
+    sfm.sfm_attention(ctx, q.to(DEV), k.to(DEV), vt[..., vt_order(Lp)].contiguous().to(DEV), o, B, L)
     torch.cuda.synchronize()
     rows = np.arange(L) if L <= 1000 else np.array([0, 1, 100, 511, 512, 2000, 4095, 4607])
     for b in range(B):
@@ -329,7 +332,7 @@ def test_attention_large_scores(sfm, ctx_tiny):
     k[:, :, :L] = kk.to(torch.bfloat16)
     vt[:, :, :, :L] = synth.bf16_normal((B, H, 256, L), ("lv",), 1.0).to(torch.float16)
     o = torch.empty(B * L, H * 256, dtype=torch.bfloat16, device=DEV)
-    sfm.sfm_attention(ctx_tiny, q.to(DEV), k.to(DEV), vt.to(DEV), o, B, L)
+    sfm.sfm_attention(ctx_tiny, q.to(DEV), k.to(DEV), vt[..., vt_order(Lp)].contiguous().to(DEV), o, B, L)
     torch.cuda.synchronize()
     ref = N.bf16_round(O.attention(np64(q[0, :, :L]).transpose(1, 0, 2), np64(k[0, :, :L]).transpose(1, 0, 2),
                                    np64(vt[0, :, :, :L]).transpose(2, 0, 1))).reshape(L, -1)
