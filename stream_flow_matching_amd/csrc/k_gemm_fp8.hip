@@ -9,21 +9,23 @@
 // silu(gate) * up with the gate and up rows of one output column computed by
 // the same lane.
 //
-// Structure: one workgroup of four waves (2 x 2) computes a BM x BN tile; K is
-// walked in steps of 128 bytes.  Both operand tiles go global -> LDS with
-// buffer_load ... lds (no staging registers), two stages, one barrier per
-// step; every 1 KiB wave-load covers 8 rows of 128 bytes and applies the XOR
-// swizzle (16-byte chunk ^ ((row >> 1) & 7)) through its source offsets: the
-// LDS serves 256 bytes (64 banks) per clock, two 128-byte rows per bank line,
-// and the swizzle puts the 16 rows that one MFMA operand read touches into 16
-// distinct 16-byte bank slots.  Rows past
-// M are clamped to row M - 1 for loading (their results are never stored).
-// Each wave issues v_mfma_f32_16x16x128_f8f6f4 on 16x16 sub-tiles: A operand
-// = 16 token rows x 128 k, B operand = 16 weight rows x 128 k; lane l holds
-// rows (l & 15) and the 32-byte k-slice (l >> 4) of both, so the product is
-// independent of how the instruction orders k inside a lane.  Output lane l
-// holds rows 4*(l>>4)+r, column l & 15.  Tiles are numbered XCD by XCD and, in
-// each XCD's range, in 8-row groups (L2 reuse of both operands).
+// Structure: one workgroup of four waves (2 x 2) computes a BM x BN tile.  K
+// is walked in stages of 128 bytes held in a two-stage LDS ring; operand tiles
+// go global -> LDS with buffer_load ... lds (no staging registers).  Each stage
+// is two halves of 64 k, one v_mfma_f32_32x32x64_f8f6f4 deep, and the
+// fragments of a half are read from LDS while the matrix cores work on the
+// previous half (two register sets), so the MFMA stream does not wait on LDS.
+// There is one barrier per stage, after the waves have read the stage's last
+// half: it frees the stage for the load two stages ahead, whose 1 KiB
+// wave-loads are interleaved one by one with the MFMAs that follow.  Every
+// wave-load covers 8 rows of 128 bytes; its source offsets apply the XOR
+// swizzle 16-byte chunk ^ ((row >> 1) & 7), which puts the 16 rows that one
+// quarter of a ds_read_b128 touches into 16 distinct 16-byte slots of the 64
+// LDS banks.  Rows past M are clamped to row M - 1 for loading (their results
+// are never stored).  MFMA operands: lane l holds row (l & 31) and the same
+// 32-byte k-slice (l >> 5) of A and W, so the product does not depend on how
+// the instruction orders k inside a lane.  Tiles are numbered XCD by XCD and,
+// in each XCD's range, in 8-row groups (L2 reuse of both operands).
 #include "gemm_common.h"
 
 namespace sfm {
@@ -35,30 +37,34 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define SFM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kBK = 128;
+constexpr int kBK = 128;  // k bytes per stage
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kGroupM = 8;
 
-// Direct global -> LDS loads of one pipeline stage: AI wave-loads of the A
-// tile and BI of the weight tile, 1 KiB each (lane l writes bytes 16 l .. 16 l + 15).
-template <int AI, int BI>
-struct StageLoader {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    const uint32_t* aoff;
-    const uint32_t* boff;
-    uint32_t lds0;   // this wave's first 1 KiB block
-    uint32_t bbase;  // byte offset of the weight tile inside a stage
+// s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (expcnt not waited on)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
 
-    __device__ __forceinline__ void issue(uint8_t* stage, int k0) const {
-#pragma unroll
-        for (int i = 0; i < AI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, SFM_LDS(stage + lds0 + i * 4096), 16, aoff[i], k0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, SFM_LDS(stage + bbase + lds0 + i * 4096), 16, boff[i], k0, 0,
-                                                     0);
-    }
-};
+// Workgroup barrier for LDS that has already been waited for (wait_vm_lgkm0):
+// the empty asm statements keep the compiler from moving LDS accesses across
+// it, and no fence is used because a fence would also drain the loads still
+// in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One 1 KiB wave-load: lane l copies 16 bytes from byte voff + soff of the
+// buffer to LDS bytes lds + 16 l .. lds + 16 l + 15.  (A free function: the
+// address-space cast inside a lambda of a kernel template loses the kernel's
+// host-side stub.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SFM_LDS(lds), 16, voff, soff, 0, 0);
+}
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(
@@ -66,99 +72,122 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float* __restrict__ sw, uint16_t* out, const uint16_t* resid, const float* __restrict__ gate,
     int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn) {
     constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
-    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int AI = BM / 32, BI = BN / 32;  // 1 KiB wave-loads per stage per wave
+    constexpr int NV = AI + BI;                // vector-memory ops per stage per wave
+    constexpr int NF = FM + FN;                // fragments per half-stage
+    constexpr int NQ = (FM / 2) * FN;          // MFMAs per quarter-stage
     constexpr int STAGE = (BM + BN) * kBK;
+    static_assert(FM % 2 == 0, "quarter-stages split the row tiles in two");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
     grouped_tile(xcd_tile_id(), ntm, ntn, kGroupM, tm, tn);
     const int m0 = tm * BM;
 
-    // per-lane source offsets: wave-load i of this wave covers tile rows 8 (wave + 4 i) + (lane >> 3),
-    // physical chunk lane & 7 holding logical chunk (lane & 7) ^ ((row >> 1) & 7), where
-    // (row >> 1) & 7 = (4 (wave & 1) + (lane >> 4)) & 7 for every i
+    // wave-load v of this wave covers tile rows 8 (wave + 4 v) + (lane >> 3); the lane writes
+    // physical chunk lane & 7, which holds logical chunk (lane & 7) ^ ((row >> 1) & 7), and
+    // (row >> 1) & 7 == (4 (wave & 1) + (lane >> 4)) & 7 for every v
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0x7FFFFFFF, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, 0x7FFFFFFF, kRsrcWord3);
+    // zero-length views: loads through them touch no memory (the tail stages)
+    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, 0, kRsrcWord3);
     const int lrow = lane >> 3, lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
-    uint32_t aoff[AI], boff[BI];
+    uint32_t voff[NV];
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-        const int row = min(m0 + 8 * (wave + 4 * i) + lrow, M - 1);
-        aoff[i] = (uint32_t)row * (uint32_t)K + lch * 16;
+    for (int v = 0; v < AI; ++v) {
+        const int row = min(m0 + 8 * (wave + 4 * v) + lrow, M - 1);
+        voff[v] = (uint32_t)row * (uint32_t)K + lch * 16;
     }
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-        const int64_t wr = weight_row<EPI, BN, TN>(8 * (wave + 4 * i) + lrow, tn, N);
-        boff[i] = (uint32_t)wr * (uint32_t)K + lch * 16;
+    for (int v = 0; v < BI; ++v) {
+        const int64_t wr = weight_row<EPI, BN, TN>(8 * (wave + 4 * v) + lrow, tn, N);
+        voff[AI + v] = (uint32_t)wr * (uint32_t)K + lch * 16;
     }
-    const StageLoader<AI, BI> ld{ra, rb, aoff, boff, (uint32_t)wave * 1024u, (uint32_t)(BM * kBK)};
-    auto issue = [&](uint8_t* stage, int k0) { ld.issue(stage, k0); };
+    // LDS destination of wave-load v inside a stage (uniform per wave)
+    auto vmem = [&](int v, uint8_t* stg, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, int k0) {
+        if (v < AI)
+            dma16(rA, stg + wave * 1024 + v * 4096, voff[v], k0);
+        else
+            dma16(rB, stg + BM * kBK + wave * 1024 + (v - AI) * 4096, voff[v], k0);
+    };
 
-    v4f acc[FM][FN];
+    v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-    const int lr = lane & 15, lg = lane >> 4;
-    // fragment rows have (row >> 1) & 7 == (lr >> 1) & 7: chunk offsets are per-lane constants
-    const int sx = (lr >> 1) & 7;
-    const int c0 = ((2 * lg) ^ sx) << 4, c1 = ((2 * lg + 1) ^ sx) << 4;
+    // fragment rows have (row >> 1) & 7 == (lr >> 1) & 7: chunk offsets are per-lane constants;
+    // half h of a 128-byte row holds logical chunks 4h .. 4h + 3
+    const int lr = lane & 31, lg = lane >> 5, sx = (lr >> 1) & 7;
+    const int cc[2][2] = {{((2 * lg) ^ sx) << 4, ((2 * lg + 1) ^ sx) << 4},
+                          {((4 + 2 * lg) ^ sx) << 4, ((4 + 2 * lg + 1) ^ sx) << 4}};
     const int arow = (wm * TM + lr) * kBK, brow = BM * kBK + (wn * TN + lr) * kBK;
 
-    auto compute = [&](const uint8_t* stg) {
-        v8i bf[FN];
+    // fragment f of a half: f < FN is weight column tile f, else row tile f - FN
+    v8i fr[2][NF];
+    auto ds = [&](int set, int f, const uint8_t* stg, int h) {
+        const uint8_t* p = stg + (f < FN ? brow + f * 32 * kBK : arow + (f - FN) * 32 * kBK);
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + cc[h][0]);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + cc[h][1]);
+        fr[set][f] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    auto mfma = [&](int set, int q, int i0) {
+        const int i = i0 + q / FN, j = q % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][FN + i], fr[set][j], acc[i][j], 0, 0, 0,
+                                                                    0, 0, 0);
+    };
+    // quarter-stage: NQ MFMAs on fragment set `set`, row tiles i0 .. i0 + FM/2, with the
+    // fragment reads for set `rset` from half rh of rstg (if RD) and the NV wave-loads into
+    // lstg (if LD) spread over them
+    auto quarter = [&](int set, int i0, bool RD, int rset, const uint8_t* rstg, int rh, bool LD, uint8_t* lstg,
+                       __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, int k0) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const uint8_t* p = stg + brow + j * 16 * kBK;
-            const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + c0);
-            const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + c1);
-            bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
-        // A fragments one row-tile ahead; the scheduling barriers keep the
-        // compiler from hoisting all of them (register pressure)
-        v8i af[2];
-        auto load_af = [&](int slot, int i) {
-            const uint8_t* p = stg + arow + i * 16 * kBK;
-            const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + c0);
-            const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + c1);
-            af[slot] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        };
-        load_af(0, 0);
+        for (int q = 0; q < NQ; ++q) {
+            mfma(set, q, i0);
+            if (LD)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            if (i + 1 < FM) load_af((i + 1) & 1, i + 1);
+                for (int v = q * NV / NQ; v < (q + 1) * NV / NQ; ++v) vmem(v, lstg, rA, rB, k0);
+            if (RD)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] =
-                    __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) ds(rset, f, rstg, rh);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    uint8_t* st0 = smem;
-    uint8_t* st1 = smem + STAGE;
-    // K % 256 == 0 (checked by the caller): an even number of 128-byte steps,
-    // so the two-stage loop has a single exit
-    const int nk = K / kBK;
-    issue(st0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        issue(st1, (kt + 1) * kBK);
-        compute(st0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 2 < nk) issue(st0, (kt + 2) * kBK);
-        compute(st1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
+    // K % 256 == 0 (checked by the caller): nks >= 2 and even
+    const int nks = K / kBK;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) vmem(v, smem, ra, rb, 0);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) vmem(v, smem + STAGE, ra, rb, kBK);
+    wait_vm_lgkm0<NV>();
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
 
-    gemm_epilogue<EPI, BN, TN, FM, FN>(
+    // stage t: set 0 holds half 0 of stage t on entry and half 0 of stage t + 1 on exit
+    for (int t = 0; t < nks; ++t) {
+        uint8_t* cur = smem + (t & 1) * STAGE;
+        const uint8_t* nxt = smem + ((t + 1) & 1) * STAGE;
+        const bool more = t + 2 < nks;
+        const __amdgpu_buffer_rsrc_t rA = more ? ra : ra0;
+        const __amdgpu_buffer_rsrc_t rB = more ? rb : rb0;
+        quarter(0, 0, false, 1, cur, 1, false, cur, rA, rB, 0);
+        quarter(0, FM / 2, true, 1, cur, 1, false, cur, rA, rB, 0);
+        quarter(1, 0, false, 0, cur, 0, false, cur, rA, rB, 0);
+        wait_vm_lgkm0<0>();  // stage t + 1 has landed; this wave's reads of stage t are done
+        lds_barrier();       // ... and every wave's
+        quarter(1, FM / 2, true, 0, nxt, 0, true, cur, rA, rB, (t + 2) * kBK);
+    }
+    wait_vm_lgkm0<0>();
+
+    gemm_epilogue32<EPI, BN, TN, FM, FN>(
         acc, m0 + wm * TM, wn, tn, lane, M, N, L, out, resid, gate, gate_stride,
         [&](int row) { return sa[row]; }, [&](int64_t col) { return sw[col]; });
 }
@@ -169,7 +198,7 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = 2 * (BM + BN) * kBK;
+    const size_t shm = (size_t)2 * (BM + BN) * kBK;
     auto kern = gemm_fp8_kernel<BM, BN, EPI>;
     static bool attr_set = false;
     if (!attr_set) {
