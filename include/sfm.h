@@ -178,7 +178,8 @@ typedef enum sfm_epilogue {
  * NF4 weights: a = bf16 [M][k], a_scale unused; y = a * bf16(w)^T on bf16
  * matrix cores, the NF4 decode fused into the weight-operand load.
  * gate: fp32, row b of the batch at gate + b*gate_batch_stride (n values);
- * L gives the batch of a row (b = m / L).  k % 256 == 0, n % 256 == 0. */
+ * L gives the batch of a row (b = m / L); with the gated residual and rows in
+ * more than one batch (M > L), L >= 128.  k % 256 == 0, n % 256 == 0. */
 int sfm_linear(const sfm_context* ctx, int epilogue, const void* a, const float* a_scale, const sfm_qweight* w,
                uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_batch_stride, int M, int L,
                void* stream);

@@ -15,9 +15,11 @@
 // is two halves of 64 k, one v_mfma_f32_32x32x64_f8f6f4 deep, and the
 // fragments of a half are read from LDS while the matrix cores work on the
 // previous half (two register sets), so the MFMA stream does not wait on LDS.
-// There is one barrier per stage, after the waves have read the stage's last
-// half: it frees the stage for the load two stages ahead, whose 1 KiB
-// wave-loads are interleaved one by one with the MFMAs that follow.  Every
+// Two barriers per stage: one after the waves have read the stage's last half,
+// which frees the stage for the loads two stages ahead, and one before the
+// next stage is read.  The 1 KiB wave-loads are interleaved one by one with the
+// MFMAs of the three quarter-stages after the first barrier, which keeps the
+// four waves' loads below the rate the CU's load path accepts.  Every
 // wave-load covers 8 rows of 128 bytes; its source offsets apply the XOR
 // swizzle 16-byte chunk ^ ((row >> 1) & 7), which puts the 16 rows that one
 // quarter of a ds_read_b128 touches into 16 distinct 16-byte slots of the 64
@@ -143,16 +145,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                     0, 0, 0);
     };
     // quarter-stage: NQ MFMAs on fragment set `set`, row tiles i0 .. i0 + FM/2, with the
-    // fragment reads for set `rset` from half rh of rstg (if RD) and the NV wave-loads into
-    // lstg (if LD) spread over them
-    auto quarter = [&](int set, int i0, bool RD, int rset, const uint8_t* rstg, int rh, bool LD, uint8_t* lstg,
-                       __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, int k0) {
+    // fragment reads for set `rset` from half rh of rstg (if RD) and wave-loads v0 .. v1 into
+    // lstg spread over them
+    auto quarter = [&](int set, int i0, bool RD, int rset, const uint8_t* rstg, int rh, int v0, int v1,
+                       uint8_t* lstg, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, int k0) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             mfma(set, q, i0);
-            if (LD)
 #pragma unroll
-                for (int v = q * NV / NQ; v < (q + 1) * NV / NQ; ++v) vmem(v, lstg, rA, rB, k0);
+            for (int v = v0 + q * (v1 - v0) / NQ; v < v0 + (q + 1) * (v1 - v0) / NQ; ++v) vmem(v, lstg, rA, rB, k0);
             if (RD)
 #pragma unroll
                 for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) ds(rset, f, rstg, rh);
@@ -171,25 +172,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
 
-    // stage t: set 0 holds half 0 of stage t on entry and half 0 of stage t + 1 on exit
+    // stage t: set 0 holds half 0 of stage t on entry and half 0 of stage t + 1 on exit.
+    // Barrier A (after the reads of half 1) frees stage t's buffer for the loads of stage
+    // t + 2, which are spread over the last three quarters; barrier B (before the reads of
+    // stage t + 1) follows the wait for this wave's loads of stage t + 1 (everything but the
+    // V1 loads of stage t + 2 issued since).
+    constexpr int V1 = (NV + 2) / 3, V2 = (2 * NV + 2) / 3;
     for (int t = 0; t < nks; ++t) {
         uint8_t* cur = smem + (t & 1) * STAGE;
         const uint8_t* nxt = smem + ((t + 1) & 1) * STAGE;
         const bool more = t + 2 < nks;
         const __amdgpu_buffer_rsrc_t rA = more ? ra : ra0;
         const __amdgpu_buffer_rsrc_t rB = more ? rb : rb0;
-        quarter(0, 0, false, 1, cur, 1, false, cur, rA, rB, 0);
-        quarter(0, FM / 2, true, 1, cur, 1, false, cur, rA, rB, 0);
-        quarter(1, 0, false, 0, cur, 0, false, cur, rA, rB, 0);
-        wait_vm_lgkm0<0>();  // stage t + 1 has landed; this wave's reads of stage t are done
-        lds_barrier();       // ... and every wave's
-        quarter(1, FM / 2, true, 0, nxt, 0, true, cur, rA, rB, (t + 2) * kBK);
+        const int k2 = (t + 2) * kBK;
+        quarter(0, 0, true, 1, cur, 1, 0, 0, cur, rA, rB, k2);
+        wait_vm_lgkm0<63>();
+        lds_barrier();
+        quarter(0, FM / 2, false, 1, cur, 1, 0, V1, cur, rA, rB, k2);
+        quarter(1, 0, false, 0, cur, 0, V1, V2, cur, rA, rB, k2);
+        wait_vm_lgkm0<V2>();
+        lds_barrier();
+        quarter(1, FM / 2, true, 0, nxt, 0, V2, NV, cur, rA, rB, k2);
     }
     wait_vm_lgkm0<0>();
 
-    gemm_epilogue32<EPI, BN, TN, FM, FN>(
-        acc, m0 + wm * TM, wn, tn, lane, M, N, L, out, resid, gate, gate_stride,
-        [&](int row) { return sa[row]; }, [&](int64_t col) { return sw[col]; });
+    // the ring is free once every wave is past its last read: each wave then stages its
+    // epilogue in its own quarter of the LDS
+    lds_barrier();
+    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
+                                           resid, gate, gate_stride, sa, sw);
 }
 
 template <int BM, int BN, int EPI>

@@ -486,6 +486,8 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
         SFM_CHECK(check_ptr(resid, "resid"));
         if (!gate) return fail(SFM_E_INVALID_ARG, "gate is NULL");
         if (M > L && gate_stride < w->n) return fail(SFM_E_INVALID_ARG, "gate_batch_stride < n");
+        if (M > L && L < 128)
+            return fail(SFM_E_SHAPE, "gated residual over several batches needs L >= 128 (L = %d)", L);
     }
     SFM_LAUNCH(gemm(ctx, epi, a, a_scale, w, out, resid, gate, gate_stride, M, L, (hipStream_t)stream));
     return SFM_OK;
