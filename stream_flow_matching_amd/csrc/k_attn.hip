@@ -71,6 +71,15 @@ struct Loader {
     }
 };
 
+// max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes holding one query
+// column), with the cross-row lane swaps instead of LDS permutes
+__device__ __forceinline__ float col_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ o, int L, int Lp, int H, int nqb) {
@@ -184,8 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int t4 = 1; t4 < 4; ++t4)
                 mx = fmaxf(mx, fmaxf(fmaxf(s[qt][t4][0], s[qt][t4][1]), fmaxf(s[qt][t4][2], s[qt][t4][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            mx = col_max(mx);
             const float mnew = fmaxf(mrun[qt], mx * cs);
             if (__builtin_amdgcn_ballot_w64(mnew > mrun[qt] + 8.0f) != 0) {
                 const float alpha = exp2f(mrun[qt] - mnew);
