@@ -21,7 +21,30 @@ FP8-E4M3 / NF4 weight codes).  Citations name the source page and its section:
              (4608-d projected text features) and "Validation" (separate
              image-only unconditional transformer).
 
-Parity status per function is listed in ``oracle/PINS.md``.
+What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py):
+  bf16_round / bits      torch's bfloat16 cast, ties-to-even cases
+  e4m3_decode / encode   all 256 codes vs torch's float8_e4m3fn cast; brute-force
+                         nearest-code search; saturation
+  nf4_codebook           endpoints -1, 0, 1; levels are evenly spaced normal
+                         quantiles (scipy's inverse CDF)
+  nf4/fp8 dequant        brute force per element
+  silu, timestep_embedding   closed forms
+  rms_normalize, adaln_norm  invariants (unit RMS, scale invariance, scale -1 -> 0)
+  quantize_rows_e4m3, fp8_linear  identity on representable rows, brute-force
+                         matmul when quantisation is exact, zero rows, power-of-two
+                         scaling, bounded quantisation error
+  positions, mrope_*     layout written out, closed-form angles, pair norms,
+                         identity at position 0, relative-position property,
+                         one axis moves one section
+  attention              brute force on tiny sequences, special cases
+  block_forward          gate 0 and scale -1 identities, row-subset and batch
+                         consistency
+  model_velocity         zero-layer reduction to the final layer of the embedding
+  euler_cfg, cfg_step    closed forms; uncond ignores text; guidance 1 gives cond
+  param_count            the ~9.3B of the spec table
+Parity unpinned: the whole model against a real checkpoint (none exists here);
+the modulation chunk order, the timestep MLP and the final layer are readings
+of prose, pinned only structurally.
 """
 
 from . import numerics, dit  # noqa: F401
