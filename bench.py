@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the single-block workloads")
     ap.add_argument("--cpu-sample", default="block_1024", help="workload timed on the CPU oracle")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only the dominant launch and a calibration copy (for rocprofv3 --pmc passes)")
     return ap.parse_args()
 
 
@@ -62,6 +64,10 @@ def time_gpu(fn, iters, warmup=1):
 
 
 def cfg_step_bench(sfm, synth, ctx, steps, warmup):
+    """Times `steps` CFG steps between two synchronisations; the last timed step
+    also records HIP events around each of its gate/up projection launches
+    (sfm_cfg_step_timed), which gives that kernel's launch durations inside the
+    timed region."""
     import torch
     w = synth.WORKLOADS["cfg_step_1024"]
     cond = synth.model_params(w.shape, w.layers, (0, "cond"), device="cuda")
@@ -70,6 +76,11 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup):
     cm, um = sfm.ModelWeights(cond), sfm.ModelWeights(unc)
     ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw))
     zo = torch.empty_like(z)
+    nev = 2 * w.layers
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    eve = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    for ev in evb + eve:       # creates the HIP events
+        ev.record()
 
     def step():
         sfm.sfm_cfg_step(ctx, cm, um, text, z, zo, t, dt, 4.0, w.B, w.T, w.gh, w.gw, ws)
@@ -78,14 +89,16 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(steps - 1):
         step()
+    rec = sfm.sfm_cfg_step_timed(ctx, cm, um, text, z, zo, t, dt, 4.0, w.B, w.T, w.gh, w.gw, ws, evb, eve)
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
+    launches = [evb[i].elapsed_time(eve[i]) * 1e3 for i in range(rec)]   # microseconds
     ok = bool(torch.isfinite(zo).all())
     del cond, unc, cm, um, ws
     torch.cuda.empty_cache()
-    return sec, ok
+    return sec, ok, launches[:w.layers], launches[w.layers:]
 
 
 def block_bench(sfm, synth, ctx, name, iters=5):
@@ -104,25 +117,79 @@ def block_bench(sfm, synth, ctx, name, iters=5):
             "weights": w.wfmt}
 
 
-def gemm_roofline(sfm, synth, ctx, iters=20):
-    """Dominant kernel: the FP8 gate/up projection with the SwiGLU epilogue at
-    the conditional 1024^2 shape (M 4608, N 2 x 12288, K 4608), the largest
-    single launch of the step.  Timed with HIP events on the launch stream."""
+ROOF_SHAPE = (4608, 4608, 12288)   # M, K, F of the dominant launch (gate/up + SwiGLU, conditional pass)
+ROOF_SOURCES = ("stream_flow_matching_amd/csrc/k_gemm_fp8.hip", "stream_flow_matching_amd/csrc/gemm_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_swiglu_4608x24576x4608_traffic.md")
+COPY_BYTES = 256 << 20            # plain copy kernel used to calibrate the byte counters
+
+
+def roof_operands(sfm, synth):
     import torch
-    M, K, F = 4608, 4608, 12288
+    M, K, F = ROOF_SHAPE
     g = torch.Generator(device="cuda").manual_seed(7)
     a = torch.randint(0, 0x7E, (M, K), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
     sa = torch.full((M,), 1e-3, device="cuda")
     wq, wsc = synth.fp8_weight(2 * F, K, ("roof",), device="cuda")
-    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, wq, wsc)
     out = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
-    sec = time_gpu(lambda: sfm.sfm_linear(ctx, sfm.SFM_EPI_SWIGLU, a, sa, w, out, M=M, L=M), iters, warmup=3)
+    return a, sa, wq, wsc, out
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ROOF_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain copy of
+    COPY_BYTES), or None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = next(json.loads(l.split("traffic-record:", 1)[1]) for l in f if "traffic-record:" in l)
+    except (OSError, StopIteration, ValueError):
+        return None
+    if rec.get("sources_sha256_16") != sources_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def gemm_roofline(cond_us, uncond_us):
+    """Dominant kernel: the FP8 gate/up projection with the SwiGLU epilogue
+    (gemm_fp8_kernel<256, 256, SWIGLU>), the largest launch of the step.
+    Algorithmic work 2*M*N*K per launch at the conditional shape (M 4608,
+    N 2 x 12288, K 4608); its average duration over the 34 conditional launches
+    of the last timed step, from HIP events recorded on the launch stream."""
+    M, K, F = ROOF_SHAPE
+    us = sum(cond_us) / len(cond_us)
     flops = 2.0 * M * K * 2 * F
-    achieved = flops / sec / 1e12
+    achieved = flops / (us * 1e-6) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "gemm_fp8_kernel (SwiGLU epilogue), M 4608 N 24576 K 4608",
-            "avg_launch_us": round(sec * 1e6, 2), "flop_per_launch": flops}
+            "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
+            "kernel": "gemm_fp8_kernel<256, 256, SWIGLU>, M 4608 N 24576 K 4608 (conditional pass)",
+            "avg_launch_us": round(us, 2), "launches": len(cond_us), "flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": M * K + 2 * F * K + 2 * F * 4 + M * 4 + M * F * 2,
+            "uncond_avg_launch_us": round(sum(uncond_us) / max(len(uncond_us), 1), 2)}
+
+
+def pmc_probe(sfm, synth, ctx, iters=10):
+    """Only the dominant launch and a plain device copy of COPY_BYTES, for the
+    FETCH_SIZE / WRITE_SIZE counter passes (run under rocprofv3 --pmc)."""
+    import torch
+    M, K, F = ROOF_SHAPE
+    a, sa, wq, wsc, out = roof_operands(sfm, synth)
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, wq, wsc)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(iters):
+        sfm.sfm_linear(ctx, sfm.SFM_EPI_SWIGLU, a, sa, w, out, M=M, L=M)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": "done", "copy_bytes": COPY_BYTES, "sources_sha256_16": sources_digest()}))
 
 
 def cpu_baseline(sample):
@@ -164,13 +231,16 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     ctx = sfm.Context("ideogram4", 0)
+    if args.pmc_probe:
+        pmc_probe(sfm, synth, ctx)
+        return
 
     w = synth.WORKLOADS["cfg_step_1024"]
-    sec, ok = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup)
+    sec, ok, gu_cond, gu_uncond = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup)
     tokens = w.layers * (w.B * (w.T + w.gh * w.gw) + w.B * w.gh * w.gw)
     flops = w.layers * (block_flops(w.T + w.gh * w.gw, w.B) + block_flops(w.gh * w.gw, w.B))
     step_tflops = flops / sec / 1e12
-    roof = gemm_roofline(sfm, synth, ctx)
+    roof = gemm_roofline(gu_cond, gu_uncond)
     extra = {}
     if not args.no_extra:
         for name in ("block_1024", "block_2048", "block_6to1_nf4"):

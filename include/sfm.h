@@ -260,6 +260,18 @@ int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sf
                  const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
                  int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream);
 
+/* sfm_cfg_step with launch timing, for measuring the gate/up projection inside
+ * a timed step.  ev_begin[i] / ev_end[i] are HIP events (hipEvent_t, created
+ * and owned by the caller) that are recorded on `stream` immediately before and
+ * after the i-th gate/up projection launch of the step (conditional layers
+ * first, then unconditional), for i < n_events; later launches are not
+ * bracketed.  *n_recorded (if not NULL) receives the number of pairs recorded.
+ * Errors as sfm_cfg_step, plus SFM_E_INVALID_ARG for NULL events. */
+int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                       const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
+                       int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
+                       void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded);
+
 /* ---------------------------------------------------------------- errors */
 const char* sfm_status_string(int status);
 const char* sfm_last_error(void);

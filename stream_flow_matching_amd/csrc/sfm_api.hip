@@ -207,9 +207,22 @@ hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa,
         if (e_ != hipSuccess) return fail(SFM_E_DEVICE, "launch %s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
+// Caller-owned HIP events recorded around the gate/up projection launches
+// (sfm_cfg_step_timed); pairs are used in launch order until they run out.
+struct LaunchTimer {
+    void* const* begin;
+    void* const* end;
+    int n;
+    int used;
+};
+
 // Enqueue one block; arguments already checked.
 int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
-              const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st) {
+              const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, LaunchTimer* timer = nullptr) {
+    const bool timed = timer && timer->used < timer->n;
+    auto mark = [&](void* const* ev) -> hipError_t {
+        return timed ? hipEventRecord((hipEvent_t)ev[timer->used], st) : hipSuccess;
+    };
     const sfm_dims* d = &ctx->dims;
     const int L = T + gh * gw, M = B * L, D = d->emb_dim, F = d->intermediate, H = d->num_heads;
     const int64_t ms = 4 * (int64_t)D;
@@ -230,13 +243,19 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
         SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
         SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
         SFM_LAUNCH(launch_adaln_fp8(x_out, L, 0, L, b.mod + 2 * D, ms, b.hq, b.hs, B, D, d->eps, st));
+        SFM_LAUNCH(mark(timed ? timer->begin : nullptr));
         SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(mark(timed ? timer->end : nullptr));
+        if (timed) ++timer->used;
         SFM_LAUNCH(launch_quant_rows(s, M, F, b.oq, b.os, st));
         SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
     } else {
         SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.o, nullptr, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
         SFM_LAUNCH(launch_adaln_bf16(x_out, L, 0, L, b.mod + 2 * D, ms, b.h, B, D, d->eps, st));
+        SFM_LAUNCH(mark(timed ? timer->begin : nullptr));
         SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.h, nullptr, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(mark(timed ? timer->end : nullptr));
+        if (timed) ++timer->used;
         SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, s, nullptr, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
     }
     return SFM_OK;
@@ -285,7 +304,7 @@ int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
 }
 
 int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent, float t,
-              float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st) {
+              float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st, LaunchTimer* timer = nullptr) {
     const sfm_dims* d = &ctx->dims;
     const int N = gh * gw, L = T + N, D = d->emb_dim, A = d->adaln_dim, C = d->latent_ch;
     StepWs w = plan_model(d, B, T, gh, gw, ws);
@@ -295,7 +314,7 @@ int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_
     if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
     SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
     for (int i = 0; i < mw->num_layers; ++i)
-        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st));
+        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, timer));
     SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
     SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
     SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
@@ -594,9 +613,11 @@ int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, cons
     return run_model(ctx, mw, text, latent, t, v_out, B, T, gh, gw, ws, (hipStream_t)stream);
 }
 
-int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
-                 const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B, int T,
-                 int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+             const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B, int T, int gh,
+             int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream, LaunchTimer* timer) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
     SFM_CHECK(check_model_weights(&ctx->dims, cond));
@@ -619,10 +640,34 @@ int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sf
     if (v_c_out) vc = v_c_out;
     if (v_u_out) vu = v_u_out;
     const hipStream_t st = (hipStream_t)stream;
-    SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws, st));
-    SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws, st));
+    SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws, st, timer));
+    SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws, st, timer));
     SFM_LAUNCH(launch_euler_cfg(z, vc, vu, z_out, nullptr, (int64_t)n, guidance, dt, st));
     return SFM_OK;
+}
+
+}  // namespace
+
+int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                 const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B, int T,
+                 int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream) {
+    return cfg_step(ctx, cond, uncond, text, z, z_out, t, dt, guidance, B, T, gh, gw, v_c_out, v_u_out, ws, ws_bytes,
+                    stream, nullptr);
+}
+
+int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                       const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
+                       int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
+                       void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded) {
+    if (n_events < 0 || (n_events > 0 && (!ev_begin || !ev_end)))
+        return fail(SFM_E_INVALID_ARG, "event arrays are NULL or n_events < 0");
+    for (int i = 0; i < n_events; ++i)
+        if (!ev_begin[i] || !ev_end[i]) return fail(SFM_E_INVALID_ARG, "event pair %d is NULL", i);
+    LaunchTimer timer{ev_begin, ev_end, n_events, 0};
+    const int st = cfg_step(ctx, cond, uncond, text, z, z_out, t, dt, guidance, B, T, gh, gw, v_c_out, v_u_out, ws,
+                            ws_bytes, stream, &timer);
+    if (n_recorded) *n_recorded = timer.used;
+    return st;
 }
 
 }  // extern "C"

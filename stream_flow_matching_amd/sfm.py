@@ -88,6 +88,9 @@ SIGNATURES = {
                                 _P]),
     "sfm_cfg_step": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P, _F,
                           _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "sfm_cfg_step_timed": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
+                                _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P),
+                                ctypes.POINTER(_P), _I, ctypes.POINTER(_I)]),
     "sfm_status_string": (ctypes.c_char_p, [_I]),
     "sfm_last_error": (ctypes.c_char_p, []),
 }
@@ -263,6 +266,23 @@ def sfm_cfg_step(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, 
                               _ptr(z), _ptr(z_out), float(t), float(dt), float(guidance), B, T, gh, gw,
                               _ptr(v_c_out), _ptr(v_u_out), _ptr(ws), ws.numel() * ws.element_size(),
                               _stream(stream)))
+
+
+def sfm_cfg_step_timed(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, t, dt, guidance, B, T, gh, gw,
+                       ws, ev_begin, ev_end, v_c_out=None, v_u_out=None, stream=None):
+    """sfm_cfg_step with torch.cuda.Event pairs recorded around the gate/up
+    projection launches (the events must have been recorded once, so that
+    their HIP handles exist).  Returns the number of pairs recorded."""
+    n = min(len(ev_begin), len(ev_end))
+    arr = ctypes.c_void_p * max(n, 1)
+    b = arr(*[ctypes.c_void_p(e.cuda_event) for e in ev_begin[:n]])
+    e = arr(*[ctypes.c_void_p(x.cuda_event) for x in ev_end[:n]])
+    rec = ctypes.c_int(0)
+    _check(lib().sfm_cfg_step_timed(ctx.handle, ctypes.byref(cond.c), ctypes.byref(uncond.c),
+                                    _ptr(text) if T > 0 else None, _ptr(z), _ptr(z_out), float(t), float(dt),
+                                    float(guidance), B, T, gh, gw, _ptr(v_c_out), _ptr(v_u_out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream), b, e, n, ctypes.byref(rec)))
+    return rec.value
 
 
 def workspace(nbytes, device="cuda"):

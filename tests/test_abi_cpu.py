@@ -120,6 +120,11 @@ def test_validation_happens_before_any_launch(S):
     assert L.sfm_linear(None, 0, good, good, None, good, None, None, 0, 4, 4, None) == -1
     assert L.sfm_attention(None, good, good, good, good, 1, 10, None) == -1
     assert L.sfm_block_forward(None, None, good, good, good, 1, 0, 16, 16, good, 0, None) == -1
+    nul = (ctypes.c_void_p * 1)(None)
+    assert L.sfm_cfg_step_timed(None, None, None, None, good, good, 0.5, 0.1, 4.0, 1, 0, 16, 16, None, None, good,
+                                0, None, None, None, 1, None) == -1
+    assert L.sfm_cfg_step_timed(None, None, None, None, good, good, 0.5, 0.1, 4.0, 1, 0, 16, 16, None, None, good,
+                                0, None, nul, nul, 1, None) == -1
 
 
 def test_context_creation_without_a_gpu_fails_cleanly(S):

@@ -485,6 +485,33 @@ def test_model_velocity_uncond_matches_step(sfm, ctx_tiny):
     assert rel_l2(v.cpu().numpy(), ref) < 2e-2
 
 
+def test_cfg_step_timed_matches_untimed(sfm, ctx_tiny):
+    """The timing variant brackets the gate/up launches with the caller's events
+    (one pair per layer and pass, up to the number given) and changes nothing
+    in the result."""
+    _say("cfg step timed")
+    w = synth.Workload("tiny_timed", synth.TINY, 1, 16, 16, 16, layers=3)
+    cond = synth.model_params(w.shape, 3, (0, "tiny_tc"))
+    unc = synth.model_params(w.shape, 3, (0, "tiny_tu"))
+    text, z, t, dt = synth.step_inputs(w)
+    cm, um = sfm.ModelWeights(to_device(cond)), sfm.ModelWeights(to_device(unc))
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw))
+    z0, z1, z2 = (torch.empty(1, 256, 128, device=DEV) for _ in range(3))
+    sfm.sfm_cfg_step(ctx_tiny, cm, um, text.to(DEV), z.to(DEV), z0, t, dt, 4.0, 1, w.T, w.gh, w.gw, ws)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(12)]
+    for e in evs:
+        e.record()
+    n = sfm.sfm_cfg_step_timed(ctx_tiny, cm, um, text.to(DEV), z.to(DEV), z1, t, dt, 4.0, 1, w.T, w.gh, w.gw, ws,
+                               evs[:6], evs[6:])
+    assert n == 6                      # 3 conditional + 3 unconditional layers
+    n = sfm.sfm_cfg_step_timed(ctx_tiny, cm, um, text.to(DEV), z.to(DEV), z2, t, dt, 4.0, 1, w.T, w.gh, w.gw, ws,
+                               evs[:4], evs[6:10])
+    assert n == 4                      # only as many pairs as given
+    torch.cuda.synchronize()
+    assert torch.equal(z0, z1) and torch.equal(z0, z2)
+    assert all(evs[i].elapsed_time(evs[6 + i]) > 0 for i in range(4))
+
+
 def test_cfg_step_full_properties(sfm, ctx_full):
     """The 34-layer, two-weight-set step at 1024^2 (the timed workload):
     finite, deterministic, and z' = z + dt (v_u + 4 (v_c - v_u)) holds for the
