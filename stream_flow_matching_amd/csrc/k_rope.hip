@@ -9,14 +9,19 @@
 // pass through.  cos / sin come from the context's table (computed on the host
 // in double precision, rounded to fp32), indexed by (integer position, j).
 //
-// One workgroup handles 64 tokens of one head: q and k rows are normalised and
-// rotated one wave-row at a time (lane t owns dims 2t, 2t+1 and 128+2t,
-// 128+2t+1; the rotation partner of dims 2t, 2t+1 lives in lane t ^ 32), and
-// the v slice is transposed through LDS into vt[b][h][d][token] as fp16 (every
-// bf16 value with |v| <= 65504 is exact in fp16; larger ones saturate), the
-// operand format of the attention kernel's P V product.  Inside every group of
-// 32 tokens the stored order is [4g..4g+3, 16+4g..16+4g+3] for g = 0..3: the
-// eight keys one lane of the attention kernel needs are then contiguous.
+// One workgroup handles 64 tokens of one head.  q and k rows (256 dims) are
+// processed two per wave at a time, 16 bytes per lane (lane & 31 owns dims
+// 8c .. 8c+7, c = lane & 31), four row pairs in flight per wave: the row's sum
+// of squares is reduced with DPP row rotations and a cross-row swap, and the
+// rotation partner of dims 8c.. (c < 16) is the chunk c ^ 8, one DPP row
+// rotation by 8 away.  Aligned groups of four pair indices never straddle a
+// section boundary (24 and 44 are multiples of 4), so a lane's cos / sin come
+// as two float4 loads per table.  The v slice is transposed through LDS into
+// vt[b][h][d][token] as fp16 (every bf16 value with |v| <= 65504 is exact in
+// fp16; larger ones saturate), the operand format of the attention kernel's P V
+// product.  Inside every group of 32 tokens the stored order is
+// [4g..4g+3, 16+4g..16+4g+3] for g = 0..3: the eight keys one lane of the
+// attention kernel needs are then contiguous.
 #include "sfm_internal.h"
 
 namespace sfm {
@@ -38,6 +43,34 @@ __device__ __forceinline__ int axis_pos(int l, int T, int gw, int axis) {
     return T + i % gw;
 }
 
+// x of lane (l & ~15) | ((l + 8) & 15): the chunk eight 16-byte chunks away in a 16-lane row
+__device__ __forceinline__ float ror8(float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)); }
+__device__ __forceinline__ float ror_n(float x, int n) {
+    switch (n) {
+        case 4: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, false));
+    }
+}
+// sum over the 32 lanes of each half-wave
+__device__ __forceinline__ float half_sum(float x) {
+    x += ror8(x);
+    x += ror_n(x, 4);
+    x += ror_n(x, 2);
+    x += ror_n(x, 1);
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ void unpack8(uint4 w, float (&u)[8]) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        u[2 * e] = __uint_as_float(a[e] << 16);
+        u[2 * e + 1] = __uint_as_float(a[e] & 0xFFFF0000u);
+    }
+}
+
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __restrict__ qkv,
                                                            const uint16_t* __restrict__ qn,
                                                            const uint16_t* __restrict__ kn,
@@ -54,48 +87,60 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
     const int64_t row_stride = 3 * (int64_t)D;
     const uint16_t* base = qkv + (int64_t)b * L * row_stride;
 
-    // rotary index of this lane's first pair of dims
-    const int j = (2 * lane) & 63;  // dims 2*lane, 2*lane+1 -> pair index j, j+1
-    const bool first_half = lane < 32;
-    const int axis = j < 24 ? 0 : (j < 44 ? 1 : 2);  // pairs never straddle a section boundary
+    const int c = lane & 31, hw = lane >> 5;   // 16-byte chunk of the row, which row of the pair
+    const bool rot = c < 16, first = c < 8;
+    const int j0 = 8 * (c & 7);                // pair index of this lane's first dim (rotated chunks)
+    const int axA = j0 < 24 ? 0 : (j0 < 44 ? 1 : 2), axB = j0 + 4 < 24 ? 0 : (j0 + 4 < 44 ? 1 : 2);
+    float gq[8], gk[8];
+    unpack8(*reinterpret_cast<const uint4*>(qn + 8 * c), gq);
+    unpack8(*reinterpret_cast<const uint4*>(kn + 8 * c), gk);
 
-    // q (part 0) and k (part 1): 2 * 64 rows of 256 per workgroup, one row per wave at a time
-    for (int it = wave; it < 2 * kTok; it += 4) {
-        const int part = it / kTok;
-        const int l = l0 + (it % kTok);
-        uint16_t* dst = (part == 0 ? q : k) + (((int64_t)b * H + h) * Lp + l) * 256;
-        if (l >= L) {
-            reinterpret_cast<uint32_t*>(dst)[lane] = 0u;
-            reinterpret_cast<uint32_t*>(dst + 128)[lane] = 0u;
-            continue;
+    // 128 rows (64 q then 64 k), 8 per round of the four waves, 4 rounds per batch
+    constexpr int kU = 4;
+    for (int r0 = 0; r0 < 2 * kTok; r0 += 8 * kU) {
+        float u[kU][8];
+        int lrow[kU];
+#pragma unroll
+        for (int v = 0; v < kU; ++v) {
+            const int r = r0 + 8 * v + 2 * wave + hw;
+            const int part = r / kTok, l = l0 + r % kTok;
+            lrow[v] = l;
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (l < L) w = *reinterpret_cast<const uint4*>(base + (int64_t)l * row_stride + part * D + h * 256 + 8 * c);
+            unpack8(w, u[v]);
         }
-        const uint16_t* src = base + (int64_t)l * row_stride + part * D + h * 256;
-        const uint32_t w0 = reinterpret_cast<const uint32_t*>(src)[lane];
-        const uint32_t w1 = reinterpret_cast<const uint32_t*>(src + 128)[lane];
-        float u0 = __uint_as_float(w0 << 16), u1 = __uint_as_float(w0 & 0xFFFF0000u);
-        float u2 = __uint_as_float(w1 << 16), u3 = __uint_as_float(w1 & 0xFFFF0000u);
-        const float ss = wave_sum(u0 * u0 + u1 * u1 + u2 * u2 + u3 * u3);
-        const float r = 1.0f / sqrtf(ss / 256.0f + eps);
-        const uint16_t* g = part == 0 ? qn : kn;
-        u0 = u0 * r * bf16_to_f32(g[2 * lane]);
-        u1 = u1 * r * bf16_to_f32(g[2 * lane + 1]);
-        u2 = u2 * r * bf16_to_f32(g[128 + 2 * lane]);
-        u3 = u3 * r * bf16_to_f32(g[128 + 2 * lane + 1]);
-        const float p0 = __shfl_xor(u0, 32, 64);
-        const float p1 = __shfl_xor(u1, 32, 64);
-        const int pos = axis_pos(l, T, gw, axis);
-        const float c0 = cos_t[pos * 64 + j], c1 = cos_t[pos * 64 + j + 1];
-        const float s0 = sin_t[pos * 64 + j], s1 = sin_t[pos * 64 + j + 1];
-        float o0, o1;
-        if (first_half) {  // dims j, j+1: a*cos - b*sin
-            o0 = u0 * c0 - p0 * s0;
-            o1 = u1 * c1 - p1 * s1;
-        } else {           // dims j+64, j+65: b*cos + a*sin
-            o0 = u0 * c0 + p0 * s0;
-            o1 = u1 * c1 + p1 * s1;
+#pragma unroll
+        for (int v = 0; v < kU; ++v) {
+            const int r = r0 + 8 * v + 2 * wave + hw;
+            const int part = r / kTok, l = lrow[v];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += u[v][e] * u[v][e];
+            const float rn = 1.0f / sqrtf(half_sum(ss) / 256.0f + eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[v][e] = u[v][e] * rn * (part == 0 ? gq[e] : gk[e]);
+            const int lc = min(l, L - 1);
+            const int pa = axis_pos(lc, T, gw, axA), pb = axis_pos(lc, T, gw, axB);
+            const float4 ca = *reinterpret_cast<const float4*>(cos_t + pa * 64 + j0);
+            const float4 cb = *reinterpret_cast<const float4*>(cos_t + pb * 64 + j0 + 4);
+            const float4 sa = *reinterpret_cast<const float4*>(sin_t + pa * 64 + j0);
+            const float4 sb = *reinterpret_cast<const float4*>(sin_t + pb * 64 + j0 + 4);
+            const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+            const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = ror8(u[v][e]);
+                // dims j (first half): a cos - b sin; dims j + 64: b cos + a sin
+                const float rv = first ? u[v][e] * cs[e] - p * sn[e] : u[v][e] * cs[e] + p * sn[e];
+                o[e] = rot ? rv : u[v][e];
+            }
+            uint16_t* dst = (part == 0 ? q : k) + (((int64_t)b * H + h) * Lp + l) * 256 + 8 * c;
+            uint4 pk = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                  pack_bf16x2(o[6], o[7]));
+            if (l >= L) pk = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(dst) = pk;
         }
-        reinterpret_cast<uint32_t*>(dst)[lane] = pack_bf16x2(o0, o1);
-        reinterpret_cast<uint32_t*>(dst + 128)[lane] = pack_bf16x2(u2, u3);
     }
 
     // v: load [64 tokens][256 d] (16 bytes per thread-step), store transposed into LDS
