@@ -168,6 +168,86 @@ __global__ __launch_bounds__(256) void small_linear_kernel(const void* __restric
     }
 }
 
+// out fp32 = A W^T + bias for a bf16 A (row mapping as above) and bf16 W [N][K]
+// on bf16 matrix cores: a workgroup computes 32 rows x 128 columns, wave w the
+// columns 32w .. 32w+31 as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16 (fp32
+// accumulation).  A and W fragments come straight from global memory (16
+// contiguous bytes of K per lane) in batches of four k-steps, one batch ahead.
+// K % 32 == 0.  Rows are clamped for loading, columns past N are not stored.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void bf16_linear_f32_kernel(const uint16_t* __restrict__ a, int64_t a_rpb,
+                                                              int64_t a_bs, int64_t a_off,
+                                                              const uint16_t* __restrict__ w,
+                                                              const float* __restrict__ bias, float* __restrict__ out,
+                                                              int64_t o_rpb, int64_t o_bs, int64_t o_off, int M, int N,
+                                                              int K) {
+    constexpr int kB = 4;  // k-steps of 32 per batch
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 128 + wave * 32;
+    const uint16_t* ap[2];
+    const uint16_t* wp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = min(m0 + 16 * i + lr, M - 1);
+        ap[i] = a + ((m / a_rpb) * a_bs + a_off + m % a_rpb) * K + 8 * lg;
+        const int n = min(n0 + 16 * i + lr, N - 1);
+        wp[i] = w + (int64_t)n * K + 8 * lg;
+    }
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t fa[2][kB][2], fb[2][kB][2];
+    auto load = [&](int slot, int k0) {
+#pragma unroll
+        for (int s = 0; s < kB; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int k = min(k0 + 32 * s, K - 32);
+                fa[slot][s][i] = *reinterpret_cast<const bf16x8_t*>(ap[i] + k);
+                fb[slot][s][i] = *reinterpret_cast<const bf16x8_t*>(wp[i] + k);
+            }
+    };
+    const int nb = (K / 32 + kB - 1) / kB;
+    load(0, 0);
+    for (int bt = 0; bt < nb; bt += 2) {
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int b = bt + par;
+            if (b >= nb) break;
+            if (b + 1 < nb) load(par ^ 1, (b + 1) * kB * 32);
+#pragma unroll
+            for (int s = 0; s < kB; ++s) {
+                if ((b * kB + s) * 32 >= K) break;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[par][s][i], fb[par][s][j], acc[i][j],
+                                                                            0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + 16 * j + lr;
+            if (n >= N) continue;
+            const float bn = bias ? bias[n] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * i + 4 * lg + r;
+                if (m >= M) continue;
+                out[((m / o_rpb) * o_bs + o_off + m % o_rpb) * N + n] = acc[i][j][r] + bn;
+            }
+        }
+}
+
 // dst rows b*dst_rpb + r <- src rows b*src_rpb + r, r < rows; cols % 8 == 0.
 __global__ void copy_rows_kernel(const uint16_t* __restrict__ src, int64_t src_rpb, uint16_t* __restrict__ dst,
                                  int64_t dst_rpb, int rows, int cols) {
@@ -212,6 +292,12 @@ hipError_t launch_small_linear(const void* a, int a_bf16, int64_t a_rpb, int64_t
                                const uint16_t* w, const float* bias, void* out, int out_bf16, int64_t o_rpb,
                                int64_t o_bstride, int64_t o_off, int M, int N, int K, hipStream_t st) {
     if (M == 0) return hipSuccess;
+    if (a_bf16 && !out_bf16 && K % 32 == 0) {
+        hipLaunchKernelGGL(bf16_linear_f32_kernel, dim3((M + 31) / 32, (N + 127) / 128), dim3(256), 0, st,
+                           (const uint16_t*)a, a_rpb, a_bstride, a_off, w, bias, (float*)out, o_rpb, o_bstride,
+                           o_off, M, N, K);
+        return hipGetLastError();
+    }
     const dim3 grid((M + kSL - 1) / kSL, (N + kSL - 1) / kSL);
     if (a_bf16 && out_bf16)
         hipLaunchKernelGGL((small_linear_kernel<true, true>), grid, dim3(256), 0, st, a, a_rpb, a_bstride, a_off, w,
