@@ -148,6 +148,12 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
         }
     } else {
         constexpr int NCH = TN / 4;  // 16-byte chunks (four fp32) per LDS row
+        // the two half-waves of a write are four rows apart; rows four apart start on the same
+        // bank, so every other group of four rows is shifted by eight chunks (128 bytes)
+        auto swz = [](int ch, int row) {
+            const int f = ((row >> 2) & 1) << 3;
+            return NCH % 16 == 0 ? (ch ^ f) : (ch + f) % NCH;
+        };
         const int64_t col0 = (int64_t)tn * BN + wn * TN;
         const int r_first = min(m0w, M - 1), r_last = min(m0w + TM - 1, M - 1);
         const int b_first = r_first / L, b_last = r_last / L;
@@ -173,7 +179,7 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
                         const int row = trow - p * (TM / 2);
                         const float gv = m0w + trow < row_split ? g0[j] : g1[j];
                         const float v = gv * (acc[i][j][r] * rsv[i][r] * cs[j]);
-                        const int off = row * (TN * 4) + (((c >> 2) ^ (((row >> 2) & 1) << 3)) << 4) + (c & 3) * 4;
+                        const int off = row * (TN * 4) + (swz(c >> 2, row) << 4) + (c & 3) * 4;
                         *reinterpret_cast<float*>(lds + off) = v;
                     }
                 }
@@ -194,8 +200,7 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 #pragma unroll
                 for (int s = 0; s < SB; ++s) {
                     const int q = 64 * (s0 + s) + lane, row = q / NCH, ch = q % NCH;
-                    const float4 v = *reinterpret_cast<const float4*>(lds + row * (TN * 4) +
-                                                                      ((ch ^ (((row >> 2) & 1) << 3)) << 4));
+                    const float4 v = *reinterpret_cast<const float4*>(lds + row * (TN * 4) + (swz(ch, row) << 4));
                     const int grow = m0w + p * (TM / 2) + row;
                     uint2 pk;
                     pk.x = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].x) + v.x, bf16_to_f32((uint16_t)(rv[s].x >> 16)) + v.y);

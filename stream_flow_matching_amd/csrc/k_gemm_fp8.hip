@@ -221,19 +221,37 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
     return hipGetLastError();
 }
 
+// Rounds of workgroups over the 256 compute units times the work of one tile,
+// divided by the main loop's measured efficiency at that tile shape.
+inline double tile_cost(int M, int N, int BM, int BN, double eff) {
+    const int64_t tiles = (int64_t)((M + BM - 1) / BM) * (N / BN);
+    return (double)((tiles + 255) / 256) * BM * BN / eff;
+}
+
 template <int EPI>
 hipError_t launch_epi(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
                       hipStream_t st) {
-    // 256 x 256 tiles when they give at least ~3 rounds of workgroups over the
-    // 256 compute units, else 256 x 128, else 128 x 128
-    const int64_t t256 = (int64_t)((M + 255) / 256) * (N / 256);
-    const int64_t t128 = (int64_t)((M + 255) / 256) * (N / 128);
-    if (N % 256 == 0 && t256 >= 700)
-        return launch_cfg<256, 256, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
-    if (t128 >= 400)
-        return launch_cfg<256, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
-    return launch_cfg<128, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+    // the cheapest of the tile shapes that divide N (256 x 192 for the gated residual only)
+    double best = 1e300;
+    int cfg = 3;
+    const double c256 = N % 256 == 0 ? tile_cost(M, N, 256, 256, 0.93) : 1e300;
+    const double c192 = EPI == SFM_EPI_RESID_GATE && N % 192 == 0 ? tile_cost(M, N, 256, 192, 0.92) : 1e300;
+    const double c128 = tile_cost(M, N, 256, 128, 0.81);
+    const double c64 = tile_cost(M, N, 128, 128, 0.70);
+    if (c256 < best) best = c256, cfg = 0;
+    if (c192 < best) best = c192, cfg = 1;
+    if (c128 < best) best = c128, cfg = 2;
+    if (c64 < best) best = c64, cfg = 3;
+    switch (cfg) {
+        case 0: return launch_cfg<256, 256, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+        case 1:
+            if constexpr (EPI == SFM_EPI_RESID_GATE)
+                return launch_cfg<256, 192, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+            return hipErrorInvalidValue;
+        case 2: return launch_cfg<256, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+        default: return launch_cfg<128, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+    }
 }
 
 }  // namespace

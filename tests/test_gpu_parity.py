@@ -209,6 +209,34 @@ def test_linear_fp8_full_width_sampled(sfm, ctx_full):
     assert rel_l2(np64(out[rows]), N.bf16_round(y)) < 2e-3
 
 
+@pytest.mark.parametrize("M", [4608, 4500])
+def test_linear_fp8_gated_residual_full_width(sfm, ctx_full, M):
+    """Down projection with the gated residual at the 1024^2 shape (N 4608,
+    K 12288; M ragged at 4500), in place (out == resid), two batches of rows;
+    sampled rows, including the ragged last tile, against the oracle."""
+    _say("linear fp8 resid full", M)
+    K, Nw = 12288, 4608
+    L = 2304
+    a = _rand_codes((M, K), ("lr", M))
+    sa = (torch.rand(M, generator=torch.Generator().manual_seed(3)) * 2e-3 + 1e-3).float()
+    wq, ws = synth.fp8_weight(Nw, K, ("lrw",))
+    keep = (wq.to(DEV), ws.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    resid = synth.bf16_normal((M, Nw), ("lrr", M), 1.0)
+    gate = synth.randn(((M + L - 1) // L, Nw), ("lrg", M), 0.5)
+    x = resid.to(DEV)
+    sfm.sfm_linear(ctx_full, 1, a.to(DEV), sa.to(DEV), w, x, x, gate.to(DEV), Nw, M=M, L=L)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 255, 2303, 2304, 3333, M - 5, M - 1])
+    y = (N.e4m3_decode(npu8(a[rows])) @ N.e4m3_decode(npu8(wq)).T) * sa.numpy()[rows, None].astype(np.float64) \
+        * ws.numpy()[None, :].astype(np.float64)
+    g = np64(gate)[rows // L]
+    ref = N.bf16_round(np64(resid[rows]) + g * y)
+    got = np64(x[rows])
+    assert rel_l2(got, ref) < 2e-3
+    assert rel_l2(got - np64(resid[rows]), ref - np64(resid[rows])) < 1e-2
+
+
 # --------------------------------------------------------------------------- a12 NF4 linear
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
