@@ -32,9 +32,11 @@ def sources():
 
 # Per-source code-generation options.  The attention kernel keeps its O
 # accumulators in the VGPR form of the MFMA instructions: the default mixed
-# VGPR/AGPR assignment moves them between the two register files every tile.
+# VGPR/AGPR assignment moves them between the two register files every tile;
+# no operand of its max reductions can be a NaN, so the canonicalising moves
+# around the cross-lane swaps are dropped.
 FILE_FLAGS = {
-    "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
 }
 
 

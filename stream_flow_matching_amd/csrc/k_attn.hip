@@ -10,8 +10,9 @@
 // Per tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K
 // rows, B = Q rows), so every lane holds the scores of ONE query column
 // (lane & 15) for keys 4*(lane>>4)+r: the softmax max is a reduction over the
-// lane's values and the 4 lanes sharing the column; the running sum stays a
-// per-lane partial until the end.  P^T then feeds O^T += V^T P^T directly from
+// lane's values and the 4 lanes sharing the column; the running sum of the
+// weights comes from one extra MFMA per 32 keys and query tile (a constant
+// operand whose first row is ones).  P^T then feeds O^T += V^T P^T directly from
 // registers as the B operand, and O^T's query column is again lane-local, so
 // rescaling is lane-local too.  The running max is only moved when a tile
 // raises it by more than 2^8 (scores then stay below 2^8 relative to the kept
@@ -143,7 +144,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) oacc[qt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     float mrun[2] = {-1e30f, -1e30f};
-    float lsum[2] = {0.f, 0.f};
+    // row sums of P^T come from the matrix cores: a constant A fragment whose first row is all
+    // ones (row 0 of the A operand lives in lanes 0, 16, 32, 48) turns O^T += V^T P^T into l += 1^T P^T, summing exactly the
+    // fp16 weights that O accumulates; lane l (l < 16) holds query column l in lacc[qt][0]
+    v4f lacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    f16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (_Float16)(lr == 0 ? 1.0f : 0.0f);
     const float cs = 0.0625f * 1.4426950408889634f;  // 1/sqrt(256) * log2(e)
 
     auto compute = [&](const uint8_t* stg, int key0) {
@@ -198,22 +205,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (__builtin_amdgcn_ballot_w64(mnew > mrun[qt] + 8.0f) != 0) {
                 const float alpha = exp2f(mrun[qt] - mnew);
                 mrun[qt] = mnew;
-                lsum[qt] *= alpha;
+                lacc[qt] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < 16; ++dt) oacc[qt][dt] *= alpha;
             }
             const float mref = mrun[qt];
-            float ls = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 // v_exp_f32 directly: results below 2^-126 flush to zero, which a
                 // softmax weight relative to a max of at least 1 can ignore
                 float p[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(s[qt][2 * h2 + (e >> 2)][e & 3] * cs - mref);
-                    ls += p[e];
-                }
+                for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(s[qt][2 * h2 + (e >> 2)][e & 3] * cs - mref);
                 f16x8 ph;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
@@ -223,7 +226,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
                 pf[qt][h2] = ph;
             }
-            lsum[qt] += ls;
         }
 
         // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments four d-tiles ahead
@@ -248,6 +250,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     oacc[qt][dt] =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
             }
+            if ((g & 3) == 3)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qt][h2], lacc[qt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -274,9 +280,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int D = H * kD;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        float l = lsum[qt];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = __shfl(lacc[qt][0], lr, 64);
         const float inv = 1.0f / l;
         const int qi = q0 + qt * 16 + lr;
         if (qi < L) {
