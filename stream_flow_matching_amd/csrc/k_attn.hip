@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) s[qt][t4] = v4f{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kf[2][4];
+        bf16x8 kf[3][4];
         auto load_kf = [&](int slot, int ks) {
             const int base = kb[ks & 3] + (ks >> 2) * 256;
 #pragma unroll
@@ -170,15 +170,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 kf[slot][t4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + base + t4 * 8192));
         };
         load_kf(0, 0);
+        load_kf(1, 1);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            if (ks + 1 < 8) load_kf((ks + 1) & 1, ks + 1);
+            if (ks + 2 < 8) load_kf((ks + 2) % 3, ks + 2);
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
                     s[qt][t4] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (key0 + kKB > L) {  // ragged last tile: mask keys >= L
@@ -228,8 +229,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
 
-        // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments four d-tiles ahead
-        f16x8 vf[2][4];
+        // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments two groups of four
+        // d-tiles ahead (three register slots), like the K fragments of S^T (two steps ahead)
+        f16x8 vf[3][4];
         auto load_vf = [&](int slot, int g) {  // g = 0..7: h2 = g >> 2, d-tiles 4 (g & 3) .. +3
             const int base = (g >> 2) ? vb1 : vb0;
 #pragma unroll
@@ -238,9 +240,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vl + base + (4 * (g & 3) + u) * 2048));
         };
         load_vf(0, 0);
+        load_vf(1, 1);
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
-            if (g + 1 < 8) load_vf((g + 1) & 1, g + 1);
+            if (g + 2 < 8) load_vf((g + 2) % 3, g + 2);
             const int h2 = g >> 2;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
                     oacc[qt][dt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g % 3][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
             }
             if ((g & 3) == 3)
 #pragma unroll
