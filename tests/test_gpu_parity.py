@@ -441,9 +441,10 @@ def test_block_gate_zero_is_identity(sfm, ctx_tiny):
     assert torch.equal(xo.cpu(), x)
 
 
-@pytest.mark.parametrize("name", ["block_1024", "block_6to1_nf4"])
+@pytest.mark.parametrize("name", ["block_1024", "block_6to1_nf4", "block_2048"])
 def test_block_full_sampled(sfm, ctx_full, name):
-    """Full-width blocks at their real shapes; sampled output rows against the
+    """Full-width blocks at their real shapes, up to the longest sequence
+    (2048 text + 128x128 image tokens, L 18432); sampled output rows against the
     oracle (keys / values for every token, queries and MLP for the samples)."""
     _say("block full", name)
     w = synth.WORKLOADS[name]
