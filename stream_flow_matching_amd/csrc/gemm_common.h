@@ -94,7 +94,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 //   RESID_GATE: gate * y is staged in fp32 (64 rows at a time), read back four
 //     columns per lane and added to the residual there, so the bf16 rounding of
 //     resid + gate * y happens once, as in the direct form.
-// Scales: sa[row] per token row, sw[weight row] per B-tile column; the gate row
+// Scales: sa[row] per token row, sw[weight row] per B-tile column (1 when the
+// pointer is null: operands that carry no scale); the gate row
 // of a token row is its batch m / L, and the wave's rows touch at most two
 // batches (callers guarantee L >= TM).  Rows past M are computed from the
 // clamped operand rows and not stored.  lds: 128 * TN * 2 bytes per wave
@@ -110,10 +111,11 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) rsv[i][r] = sa[min(m0w + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3), M - 1)];
+        for (int r = 0; r < 16; ++r)
+            rsv[i][r] = sa ? sa[min(m0w + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3), M - 1)] : 1.0f;
     float cs[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) cs[j] = sw[weight_row<EPI, BN, TN>(wn * TN + 32 * j + lc, tn, N)];
+    for (int j = 0; j < FN; ++j) cs[j] = sw ? sw[weight_row<EPI, BN, TN>(wn * TN + 32 * j + lc, tn, N)] : 1.0f;
 
     if constexpr (EPI == SFM_EPI_STORE || EPI == SFM_EPI_SWIGLU) {
         constexpr int OC = EPI == SFM_EPI_SWIGLU ? TN / 2 : TN;  // output columns of the wave tile

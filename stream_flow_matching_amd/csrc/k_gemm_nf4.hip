@@ -6,12 +6,23 @@
 // bf16(fp32(code[q[n][k]] * absmax[(n*K + k) / 64])); nibble 2i of a row is the
 // high nibble of byte i.  The activation is bf16 (no input quantisation).
 //
-// Structure: BM x BN tile per workgroup, K walked in steps of 64 (one NF4
-// block per weight row per step).  A (bf16) is staged global -> registers ->
-// LDS; each thread decodes 32 weights (16 packed bytes + their block's absmax)
-// into bf16 and writes them to LDS, with the 16-byte chunks XOR-swizzled by
-// (row & 7).  v_mfma_f32_16x16x32_bf16: lane l holds rows (l & 15) and the
-// 8-element k-slice (l >> 4) of both operands.
+// Structure: one workgroup of four waves (2 x 2) per BM x BN tile; K walks in
+// stages of 64 elements, which is exactly one NF4 block of every weight row.
+// Both operand tiles live in a two-stage LDS ring as bf16 rows of 128 bytes
+// with 16-byte chunks XOR-swizzled by (row >> 1) & 7.  The activation tile
+// goes global -> LDS with buffer_load ... lds; the weight tile is decoded by the
+// workgroup itself: each thread owns one weight row (two threads per row for
+// BN = 128), loads its 32 (16) packed bytes and the block's absmax a stage
+// ahead, looks the 4-bit codes up in a 16-entry fp32 codebook in LDS,
+// multiplies by the absmax and rounds to bf16 into the stage.  Each stage is
+// four 16-k substeps of v_mfma_f32_32x32x16_bf16 with the next substep's
+// fragments read during the current one; the decode of the next stage is
+// spread over the substeps so that its VALU work runs beside the matrix cores.
+// One barrier per stage, before the last substep: it certifies that every wave
+// has read the stage (which frees its buffer for the stage two ahead) and that
+// the next stage's activation tile and decoded weights are complete.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace sfm {
@@ -21,150 +32,244 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 64;          // k per step (elements)
-constexpr int kRow = kBK * 2;    // bytes per LDS row (bf16)
+#define SFM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRow + ((chunk ^ (row & 7)) << 4); }
+constexpr int kBK = 64;     // k elements per stage
+constexpr int kRowB = 128;  // LDS bytes per tile row per stage
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kGroupM = 8;
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_nf4_kernel(
+// s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (expcnt not waited on)
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// s_waitcnt with vmcnt <= VM only
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS that has already been waited for; the empty asm
+// statements keep the compiler from moving LDS accesses across it, and no
+// fence is used because a fence would also drain the loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One 1 KiB wave-load: lane l copies 16 bytes from byte voff + soff of the
+// buffer to LDS bytes lds + 16 l .. lds + 16 l + 15.  (A free function: the
+// address-space cast inside a lambda of a kernel template loses the kernel's
+// host-side stub.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SFM_LDS(lds), 16, voff, soff, 0, 0);
+}
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_nf4_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wq, const float* __restrict__ absmax, Nf4Code code,
     uint16_t* out, const uint16_t* resid, const float* __restrict__ gate, int64_t gate_stride, int M, int N, int K,
-    int L, int ntn) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 16, FN = TN / 16;
-    constexpr int ACH = BM * 8 / NT;        // 16-byte A chunks per thread per step
-    constexpr int BPT = BN * 2 / NT;        // 32-weight groups per thread per step
-    static_assert(ACH * NT == BM * 8 && BPT * NT == BN * 2, "tile / thread mismatch");
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ float lut[16];
-    // buffer b: A tile at smem + b*(BM+BN)*kRow, B tile right after it
-    auto lds_a = [&](int buf) { return smem + buf * (BM + BN) * kRow; };
-    auto lds_b = [&](int buf) { return smem + buf * (BM + BN) * kRow + BM * kRow; };
-    if (threadIdx.x < 16) lut[threadIdx.x] = code.v[threadIdx.x];
+    int L, int ntm, int ntn) {
+    constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
+    constexpr int NF = FM + FN;                // fragments per substep
+    constexpr int AI = BM / 32;                // 1 KiB activation wave-loads per stage per wave
+    constexpr int EPT = BN * kBK / 256;        // weights decoded per thread per stage
+    constexpr int TPR = kBK / EPT;             // threads per weight row
+    constexpr int EPP = EPT / 4;               // weights per decode part (four parts per stage)
+    constexpr int NW = EPT / 8;                // packed dwords per thread per stage
+    constexpr int STAGE = (BM + BN) * kRowB;
+    static_assert(TPR * BN == 256 && EPP % 8 == 0, "decode ownership");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_base[];
+    // the codebook sits at LDS offset 0 (a lookup address is just 4 q), the ring after it
+    float* lut = reinterpret_cast<float*>(lds_base);
+    uint8_t* const smem = lds_base + 1024;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int bid = xcd_tile_id();
-    const int tm = bid / ntn, tn = bid % ntn;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    grouped_tile(xcd_tile_id(), ntm, ntn, kGroupM, tm, tn);
     const int m0 = tm * BM;
-    const int kblocks = K / 64;
+    const int nks = K / kBK;
+    if (tid < 16) lut[tid] = code.v[tid];
 
-    const uint16_t* a_src[ACH];
-    int a_dst[ACH];
+    // activation tile: wave-load v covers tile rows 8 (wave + 4 v) + (lane >> 3), physical chunk
+    // lane & 7 holding logical chunk (lane & 7) ^ ((row >> 1) & 7)
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0x7FFFFFFF, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, kRsrcWord3);
+    const int lrow = lane >> 3, lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+    uint32_t voff[AI];
 #pragma unroll
-    for (int c = 0; c < ACH; ++c) {
-        const int i = tid + c * NT;
-        const int row = i >> 3, ch = i & 7;
-        a_src[c] = A + (int64_t)min(m0 + row, M - 1) * K + ch * 8;
-        a_dst[c] = swz(row, ch);
-    }
-    const uint8_t* b_src[BPT];
-    const float* b_am[BPT];
-    int b_row[BPT], b_half[BPT];
-#pragma unroll
-    for (int c = 0; c < BPT; ++c) {
-        const int i = tid + c * NT;
-        const int row = i >> 1, half = i & 1;
-        const int64_t wr = weight_row<EPI, BN, TN>(row, tn, N);
-        b_src[c] = Wq + wr * (K / 2) + half * 16;
-        b_am[c] = absmax + wr * kblocks;
-        b_row[c] = row;
-        b_half[c] = half;
+    for (int v = 0; v < AI; ++v) {
+        const int row = min(m0 + 8 * (wave + 4 * v) + lrow, M - 1);
+        voff[v] = (uint32_t)row * (uint32_t)(K * 2) + lch * 16;
     }
 
-    u32x4 ra[ACH], rb[BPT];
-    float rs[BPT];
-    auto gload = [&](int kt) {
+    // weight decode ownership: tile row br, elements eo .. eo + EPT - 1 of each stage
+    const int br = tid / TPR, eo = (tid % TPR) * EPT;
+    const int64_t wr = weight_row<EPI, BN, TN>(br, tn, N);
+    const uint8_t* wsrc = Wq + wr * (K / 2) + eo / 2;
+    const float* asrc = absmax + wr * (K / 64);
+    const int bsx = (br >> 1) & 7;
+    uint32_t nb[2][NW];
+    float am[2];
+    auto nib_load = [&](int slot, int s) {
+        s = min(s, nks - 1);
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) ra[c] = *reinterpret_cast<const u32x4*>(a_src[c] + kt * kBK);
-#pragma unroll
-        for (int c = 0; c < BPT; ++c) {
-            rb[c] = *reinterpret_cast<const u32x4*>(b_src[c] + kt * (kBK / 2));
-            rs[c] = b_am[c][kt];
+        for (int i = 0; i < NW / 4; ++i) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)s * (kBK / 2) + 16 * i);
+            nb[slot][4 * i] = x.x;
+            nb[slot][4 * i + 1] = x.y;
+            nb[slot][4 * i + 2] = x.z;
+            nb[slot][4 * i + 3] = x.w;
         }
+        am[slot] = asrc[s];
     };
-    auto lstore = [&](int buf) {
+    // part p: weights eo + EPP p .. + EPP - 1 -> EPP / 8 swizzled 16-byte chunks of row br
+    auto decode = [&](int slot, uint8_t* stg, int p) {
 #pragma unroll
-        for (int c = 0; c < ACH; ++c) *reinterpret_cast<u32x4*>(lds_a(buf) + a_dst[c]) = ra[c];
+        for (int c = 0; c < EPP / 8; ++c) {
+            const uint32_t w = nb[slot][p * (EPP / 8) + c];
+            uint32_t o[4];
 #pragma unroll
-        for (int c = 0; c < BPT; ++c) {
-            const uint32_t w[4] = {rb[c].x, rb[c].y, rb[c].z, rb[c].w};
-            // 16 bytes = 32 nibbles = weights k0 + 32*half + [0, 32), 4 chunks of 8 bf16
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t byte = (w[q4] >> (8 * e)) & 0xFFu;
-                    const float hi = lut[byte >> 4] * rs[c];   // element 2i: high nibble
-                    const float lo = lut[byte & 15] * rs[c];   // element 2i+1: low nibble
-                    o[e] = pack_bf16x2(hi, lo);
-                }
-                *reinterpret_cast<u32x4*>(lds_b(buf) + swz(b_row[c], b_half[c] * 4 + q4)) = u32x4{o[0], o[1], o[2], o[3]};
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t hi = __builtin_amdgcn_ubfe(w, 8 * e + 4, 4);  // element 2i
+                const uint32_t lo = __builtin_amdgcn_ubfe(w, 8 * e, 4);      // element 2i + 1
+                o[e] = cvt_bf16x2(lut[hi] * am[slot], lut[lo] * am[slot]);
             }
+            const int lc = (eo + EPP * p) / 8 + c;
+            *reinterpret_cast<u32x4*>(stg + BM * kRowB + br * kRowB + ((lc ^ bsx) << 4)) = u32x4{o[0], o[1], o[2], o[3]};
         }
     };
+    auto dma = [&](int v, uint8_t* stg, __amdgpu_buffer_rsrc_t r, int s) {
+        dma16(r, stg + wave * 1024 + v * 4096, voff[v], s * (kBK * 2));
+    };
 
-    v4f acc[FM][FN];
+    v16f acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = v16f{};
 
-    const int lr = lane & 15, lg = lane >> 4;
-    const int nk = K / kBK;
-    gload(0);
-    __syncthreads();  // lut visible
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const uint8_t* la = lds_a(buf);
-        const uint8_t* lb = lds_b(buf);
+    // fragments: lane l holds row (l & 31) and 16-byte chunk 2 ks + (l >> 5) of substep ks
+    const int lr = lane & 31, lg = lane >> 5, sx = (lr >> 1) & 7;
+    const int arow = (wm * TM + lr) * kRowB, brow = BM * kRowB + (wn * TN + lr) * kRowB;
+    u32x4 fr[2][NF];  // f < FN: weight column tile f, else row tile f - FN
+    auto ds = [&](int set, int f, const uint8_t* stg, int ks) {
+        const int off = ((2 * ks + lg) ^ sx) << 4;
+        fr[set][f] = *reinterpret_cast<const u32x4*>(stg + (f < FN ? brow + f * 32 * kRowB : arow + (f - FN) * 32 * kRowB) + off);
+    };
+    auto mfma = [&](int set, int q) {
+        const int i = q / FN, j = q % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[set][FN + i]),
+                                                            __builtin_bit_cast(bf16x8, fr[set][j]), acc[i][j], 0, 0, 0);
+    };
+    // substep: FM x FN MFMAs on `set`, with spread over them: the fragment reads of (rstg, rks)
+    // into rset (if RD), decode part dp of `dslot` into dstg (if DEC), wave-loads v0 .. v1 (if DM)
+    auto substep = [&](int set, bool RD, int rset, const uint8_t* rstg, int rks, bool DEC, int dslot, uint8_t* dstg,
+                       int dp, bool DM, uint8_t* mstg, __amdgpu_buffer_rsrc_t mr, int ms) {
+        constexpr int NQ = FM * FN;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 bfr[FN];
+        for (int q = 0; q < NQ; ++q) {
+            mfma(set, q);
+            if (DM)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                bfr[j] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(lb + swz(wn * TN + j * 16 + lr, ks * 4 + lg)));
+                for (int v = q * AI / NQ; v < (q + 1) * AI / NQ; ++v) dma(v, mstg, mr, ms);
+            if (RD)
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const bf16x8 afr = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(la + swz(wm * TM + i * 16 + lr, ks * 4 + lg)));
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
-            }
+                for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) ds(rset, f, rstg, rks);
+            if (DEC && q == NQ / 2) decode(dslot, dstg, dp);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
+    };
 
-    gemm_epilogue<EPI, BN, TN, FM, FN>(
-        acc, m0 + wm * TM, wn, tn, lane, M, N, L, out, resid, gate, gate_stride, [](int) { return 1.0f; },
-        [](int64_t) { return 1.0f; });
+    // prologue: codebook, weights of stages 0 and 1, activations of stages 0 and 1; stage 0
+    // fully decoded, stage 1 decoded in its first part (the rest follows in stage 0)
+    nib_load(0, 0);
+    nib_load(1, 1);
+#pragma unroll
+    for (int v = 0; v < AI; ++v) dma(v, smem, ra, 0);
+#pragma unroll
+    for (int v = 0; v < AI; ++v) dma(v, smem + STAGE, ra, 1);
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) decode(0, smem, p);
+    decode(1, smem + STAGE, 0);
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+#pragma unroll
+    for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
+
+    // stage t: set 0 holds substep 0 of stage t on entry and substep 0 of stage t + 1 on exit;
+    // weights of stage t + 1 are decoded in parts 1..3 here (part 0 in stage t - 1), those
+    // of stage t + 2 are loaded here and decoded from part 0 on after the barrier
+    constexpr int NL = NW / 4 + 1;  // vector loads of one stage's packed weights and absmax
+    // the two register slots of packed weights alternate with the stage's parity (compile-time)
+    auto stage = [&](auto P, int t) {
+        constexpr int s2 = decltype(P)::value, s1 = s2 ^ 1;  // slots of stages t + 2 and t + 1
+        uint8_t* cur = smem + s2 * STAGE;
+        uint8_t* nxt = smem + s1 * STAGE;
+        const __amdgpu_buffer_rsrc_t rA = t + 2 < nks ? ra : ra0;
+        substep(0, true, 1, cur, 1, true, s1, nxt, 1, false, cur, rA, 0);
+        nib_load(s2, t + 2);
+        substep(1, true, 0, cur, 2, true, s1, nxt, 2, false, cur, rA, 0);
+        substep(0, true, 1, cur, 3, true, s1, nxt, 3, false, cur, rA, 0);
+        wait_vm_lgkm0<NL>();  // stage t + 1's activations have landed; this wave's reads and decode writes are done
+        lds_barrier();        // ... and every wave's
+        substep(1, true, 0, nxt, 0, false, s2, cur, 0, true, cur, rA, t + 2);
+        wait_vm<AI>();        // stage t + 2's packed weights (loaded before the wave-loads just issued)
+        decode(s2, cur, 0);
+    };
+    // K % 256 == 0: nks is a multiple of 4
+    for (int t = 0; t < nks; t += 2) {
+        stage(std::integral_constant<int, 0>{}, t);
+        stage(std::integral_constant<int, 1>{}, t + 1);
+    }
+    wait_vm_lgkm0<0>();
+    lds_barrier();
+    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
+                                           resid, gate, gate_stride, nullptr, nullptr);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int EPI>
 hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, const Nf4Code& code, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = 2 * (BM + BN) * kRow;
-    auto kern = gemm_nf4_kernel<BM, BN, WM, WN, EPI>;
+    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 1024;
+    auto kern = gemm_nf4_kernel<BM, BN, EPI>;
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(WM * WN * 64), shm, st, a, w, am, code, out, resid, gate,
-                       gate_stride, M, N, K, L, ntn);
+    hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), shm, st, a, w, am, code, out, resid, gate, gate_stride, M, N,
+                       K, L, ntm, ntn);
     return hipGetLastError();
+}
+
+// Rounds of workgroups over the 256 compute units times the work of one tile.
+inline double nf4_tile_cost(int M, int N, int BM, int BN) {
+    const int64_t tiles = (int64_t)((M + BM - 1) / BM) * (N / BN);
+    return (double)((tiles + 255) / 256) * BM * BN;
+}
+
+template <int EPI>
+hipError_t launch_epi(const uint16_t* a, const uint8_t* w, const float* am, const Nf4Code& code, uint16_t* out,
+                      const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
+                      hipStream_t st) {
+    const double c256 = N % 256 == 0 ? nf4_tile_cost(M, N, 256, 256) : 1e300;
+    const double c128 = nf4_tile_cost(M, N, 256, 128) * 1.15;
+    if (c256 <= c128) return launch_cfg<256, 256, EPI>(a, w, am, code, out, resid, gate, gate_stride, M, N, K, L, st);
+    return launch_cfg<256, 128, EPI>(a, w, am, code, out, resid, gate, gate_stride, M, N, K, L, st);
 }
 
 }  // namespace
@@ -175,14 +280,11 @@ hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const f
     if (M == 0) return hipSuccess;
     switch (epi) {
         case SFM_EPI_STORE:
-            return launch_cfg<128, 128, 2, 2, SFM_EPI_STORE>(a, w, absmax, code, out, resid, gate, gate_stride, M, N,
-                                                             K, L, st);
+            return launch_epi<SFM_EPI_STORE>(a, w, absmax, code, out, resid, gate, gate_stride, M, N, K, L, st);
         case SFM_EPI_RESID_GATE:
-            return launch_cfg<128, 128, 2, 2, SFM_EPI_RESID_GATE>(a, w, absmax, code, out, resid, gate, gate_stride,
-                                                                  M, N, K, L, st);
+            return launch_epi<SFM_EPI_RESID_GATE>(a, w, absmax, code, out, resid, gate, gate_stride, M, N, K, L, st);
         case SFM_EPI_SWIGLU:
-            return launch_cfg<128, 128, 2, 2, SFM_EPI_SWIGLU>(a, w, absmax, code, out, resid, gate, gate_stride, M, N,
-                                                              K, L, st);
+            return launch_epi<SFM_EPI_SWIGLU>(a, w, absmax, code, out, resid, gate, gate_stride, M, N, K, L, st);
         default:
             return hipErrorInvalidValue;
     }
