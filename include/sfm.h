@@ -70,8 +70,10 @@ typedef struct sfm_context sfm_context;
  * table for every integer position the shape limits allow, built on the host
  * in double precision and rounded to fp32, and the NF4 codebook.  Only
  * emb_dim = num_heads * 256 with head_dim 256, rope_dims 128 and
- * sum(mrope_section) = 64 are supported (else SFM_E_SHAPE).  The context is
- * immutable afterwards and may be shared by threads. */
+ * sum(mrope_section) = 64 are supported (else SFM_E_SHAPE).  It also creates
+ * the two streams and three events on which sfm_cfg_step runs its two passes
+ * side by side.  The tables never change afterwards and the context may be
+ * shared by threads. */
 int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out);
 void sfm_context_destroy(sfm_context* ctx);
 
@@ -255,7 +257,11 @@ int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, cons
  * v_u from the separate unconditional model on the image tokens only (T = 0,
  * positions (0, r, c)) (research note, "Training method": asymmetric CFG drops
  * the text tokens from the unconditional pass), then sfm_euler_cfg.
- * z_out may equal z; v_c_out / v_u_out may be NULL (then workspace is used). */
+ * z_out may equal z; v_c_out / v_u_out may be NULL (then workspace is used).
+ * The two passes are independent and run at the same time on two streams the
+ * context owns; events order them after the work already on `stream` and the
+ * Euler update after both, so the call behaves as if it ran on `stream` alone.
+ * Calls on one context from several threads enqueue one after the other. */
 int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
                  const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
                  int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream);
@@ -265,7 +271,8 @@ int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sf
  * and owned by the caller) that are recorded on `stream` immediately before and
  * after the i-th gate/up projection launch of the step (conditional layers
  * first, then unconditional), for i < n_events; later launches are not
- * bracketed.  *n_recorded (if not NULL) receives the number of pairs recorded.
+ * bracketed.  The two passes run one after the other on `stream` here, so that
+ * each bracketed launch has the GPU to itself.  *n_recorded (if not NULL) receives the number of pairs recorded.
  * Errors as sfm_cfg_step, plus SFM_E_INVALID_ARG for NULL events. */
 int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
                        const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,

@@ -420,6 +420,9 @@ int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out) {
     if (e == hipSuccess) e = hipMalloc((void**)&ctx->rope_sin, sn.size() * sizeof(float));
     if (e == hipSuccess) e = hipMemcpy(ctx->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(ctx->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipStreamCreateWithFlags(&ctx->side[i], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork, hipEventDisableTiming);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ctx->join[i], hipEventDisableTiming);
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         sfm_context_destroy(ctx);
@@ -433,6 +436,11 @@ void sfm_context_destroy(sfm_context* ctx) {
     if (!ctx) return;
     if (ctx->rope_cos) (void)hipFree(ctx->rope_cos);
     if (ctx->rope_sin) (void)hipFree(ctx->rope_sin);
+    for (int i = 0; i < 2; ++i) {
+        if (ctx->side[i]) (void)hipStreamDestroy(ctx->side[i]);
+        if (ctx->join[i]) (void)hipEventDestroy(ctx->join[i]);
+    }
+    if (ctx->fork) (void)hipEventDestroy(ctx->fork);
     delete ctx;
 }
 
@@ -595,6 +603,7 @@ size_t sfm_step_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, in
     c.take<float>(n);
     c.take<float>(n);
     c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    c.take<char>(plan_model(&ctx->dims, B, 0, gh, gw, nullptr).bytes);  // the unconditional pass's own
     return c.off + 256;
 }
 
@@ -636,12 +645,29 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
     Carve c(ws);
     float* vc = c.take<float>(n);
     float* vu = c.take<float>(n);
-    void* mws = c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    void* mws_c = c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    void* mws_u = c.take<char>(plan_model(&ctx->dims, B, 0, gh, gw, nullptr).bytes);
     if (v_c_out) vc = v_c_out;
     if (v_u_out) vu = v_u_out;
     const hipStream_t st = (hipStream_t)stream;
-    SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws, st, timer));
-    SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws, st, timer));
+    if (timer) {
+        // one pass after the other on the caller's stream, so that each timed launch runs alone
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, timer));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, timer));
+    } else {
+        // the passes are independent: each on its own stream, so that the last, partly filled
+        // round of workgroups of one pass's kernels shares the GPU with the other pass
+        sfm_context* cx = const_cast<sfm_context*>(ctx);
+        std::lock_guard<std::mutex> guard(cx->step_lock);
+        SFM_TRY_HIP(hipEventRecord(cx->fork, st));
+        for (int i = 0; i < 2; ++i) SFM_TRY_HIP(hipStreamWaitEvent(cx->side[i], cx->fork, 0));
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, cx->side[0]));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, cx->side[1]));
+        for (int i = 0; i < 2; ++i) {
+            SFM_TRY_HIP(hipEventRecord(cx->join[i], cx->side[i]));
+            SFM_TRY_HIP(hipStreamWaitEvent(st, cx->join[i], 0));
+        }
+    }
     SFM_LAUNCH(launch_euler_cfg(z, vc, vu, z_out, nullptr, (int64_t)n, guidance, dt, st));
     return SFM_OK;
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sfm.h"
 
 struct sfm_context {
@@ -14,6 +16,13 @@ struct sfm_context {
     float* rope_cos;      // device [max_pos][64] fp32
     float* rope_sin;      // device [max_pos][64] fp32
     float nf4_code[16];   // NF4 codebook (fp32), passed to kernels by value
+    // the two passes of a CFG step run on these streams at once (default priority);
+    // the fork / join events order them against the caller's stream, and the lock
+    // keeps concurrent steps on one context from interleaving their use of them
+    hipStream_t side[2] = {nullptr, nullptr};
+    hipEvent_t fork = nullptr;
+    hipEvent_t join[2] = {nullptr, nullptr};
+    std::mutex step_lock;
 };
 
 namespace sfm {
