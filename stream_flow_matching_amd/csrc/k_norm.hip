@@ -130,9 +130,11 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t*
     quant_store_row<MAXC>(v, nchunk, amax, q + m * cols, s + m);
 }
 
-// out[b][n] = sum_k w[n][k] * act(in[b][k]) + bias[n]; one wave per output row,
-// act = SiLU or identity; k % 8 == 0, k <= 64 * 8 * KCH.
+// out[b][n] = sum_k w[n][k] * act(in[b][k]) + bias[n]; each wave computes
+// kGemvR consecutive output rows (their weight rows in flight together),
+// act = SiLU or identity; k % 8 == 0, B <= kGemvB.
 constexpr int kGemvB = 8;
+constexpr int kGemvR = 4;
 __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ in, int act_silu,
                                                    const uint16_t* __restrict__ w, const float* __restrict__ bias,
                                                    float* __restrict__ out, int B, int n_out, int k) {
@@ -143,35 +145,45 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ in,
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (n >= n_out) return;
-    float acc[kGemvB];
+    const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvR;
+    if (n0 >= n_out) return;
+    float acc[kGemvR][kGemvB];
 #pragma unroll
-    for (int b = 0; b < kGemvB; ++b) acc[b] = 0.f;
+    for (int j = 0; j < kGemvR; ++j)
+#pragma unroll
+        for (int b = 0; b < kGemvB; ++b) acc[j][b] = 0.f;
     for (int k0 = lane * 8; k0 < k; k0 += 512) {
-        const uint4 u = *reinterpret_cast<const uint4*>(w + n * k + k0);
-        const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-        float wf[8];
+        uint4 u[kGemvR];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wf[2 * i] = __uint_as_float(ww[i] << 16);
-            wf[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
-        }
+        for (int j = 0; j < kGemvR; ++j)
+            u[j] = n0 + j < n_out ? *reinterpret_cast<const uint4*>(w + (n0 + j) * k + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int b = 0; b < kGemvB; ++b) {
-            if (b < B) {
+        for (int j = 0; j < kGemvR; ++j) {
+            const uint32_t ww[4] = {u[j].x, u[j].y, u[j].z, u[j].w};
+            float wf[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[b] += wf[i] * xin[b * k + k0 + i];
+            for (int i = 0; i < 4; ++i) {
+                wf[2 * i] = __uint_as_float(ww[i] << 16);
+                wf[2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int b = 0; b < kGemvB; ++b) {
+                if (b < B) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[j][b] += wf[i] * xin[b * k + k0 + i];
+                }
             }
         }
     }
 #pragma unroll
-    for (int b = 0; b < kGemvB; ++b) {
-        if (b < B) {
-            const float t = wave_sum(acc[b]);
-            if (lane == 0) out[(int64_t)b * n_out + n] = t + (bias ? bias[n] : 0.f);
+    for (int j = 0; j < kGemvR; ++j)
+#pragma unroll
+        for (int b = 0; b < kGemvB; ++b) {
+            if (b < B) {
+                const float t = wave_sum_dpp(acc[j][b]);
+                if (lane == 0 && n0 + j < n_out) out[(int64_t)b * n_out + n0 + j] = t + (bias ? bias[n0 + j] : 0.f);
+            }
         }
-    }
 }
 
 // e[b][i] = cos(1000 t f_i), e[b][half + i] = sin(1000 t f_i), f_i = 10000^(-i/half);
@@ -195,8 +207,8 @@ hipError_t launch_gemv(const float* in, int act_silu, const uint16_t* w, const f
                        int n_out, int k, hipStream_t st) {
     if (B > kGemvB) return hipErrorInvalidValue;
     const size_t shm = (size_t)B * k * sizeof(float);
-    hipLaunchKernelGGL(gemv_kernel, dim3((n_out + 3) / 4), dim3(256), shm, st, in, act_silu, w, bias, out, B, n_out,
-                       k);
+    hipLaunchKernelGGL(gemv_kernel, dim3((n_out + 4 * kGemvR - 1) / (4 * kGemvR)), dim3(256), shm, st, in, act_silu, w,
+                       bias, out, B, n_out, k);
     return hipGetLastError();
 }
 

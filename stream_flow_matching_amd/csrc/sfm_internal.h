@@ -70,6 +70,27 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Sum over the 64 lanes of a wave without LDS: DPP rotations inside each
+// row of 16 lanes, then the cross-row swaps (rows 0<->1, 2<->3, then halves).
+__device__ __forceinline__ float dpp_ror(float x, int n) {
+    switch (n) {
+        case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+        case 4: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xF, 0xF, false));
+    }
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += dpp_ror(x, 8);
+    x += dpp_ror(x, 4);
+    x += dpp_ror(x, 2);
+    x += dpp_ror(x, 1);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Reduction over a workgroup of NW waves through `red` (NW floats of LDS).
 template <int NW>
 __device__ __forceinline__ float block_sum(float v, float* red) {
