@@ -3,10 +3,14 @@
 // Research note, "Model architecture": one shared bidirectional self-attention
 // over the whole [text | image] sequence.  o = softmax(q k^T / 16) v per head.
 //
-// Layout: a workgroup owns 128 queries of one (batch, head); each of its four
-// waves owns 32 queries whose q fragments stay in registers.  Tiles of 64 keys
-// stream global -> LDS with buffer_load ... lds (no staging registers): K as
-// [key][d] and V^T as [d][key], two stages of 64 KiB, one barrier per tile.
+// Layout: a workgroup owns 128 queries of one (batch, head); each of its eight
+// waves owns 16 queries whose q fragments stay in registers (two waves per SIMD,
+// at most 256 registers each).  Tiles of 64 keys stream global -> LDS with
+// buffer_load ... lds (no staging registers): K as [key][d] and V^T as
+// [d][key], two stages of 64 KiB, one barrier per tile.  A wave raises its
+// priority while it issues matrix-core work and drops it for the softmax, so
+// the SIMD's other wave, when it is in its MFMA sections, goes first and the
+// softmax arithmetic fills the gaps.
 // Per tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K
 // rows, B = Q rows), so every lane holds the scores of ONE query column
 // (lane & 15) for keys 4*(lane>>4)+r: the softmax max is a reduction over the
@@ -54,21 +58,21 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 struct Loader {
     __amdgpu_buffer_rsrc_t rk, rv;
-    uint32_t kvoff[2];      // per-lane byte offsets inside a K tile (even / odd wave-load)
+    uint32_t kvoff;         // per-lane byte offset inside a K tile
     uint32_t vvoff;         // per-lane byte offset inside a V^T tile
     uint32_t lds0;          // this wave's first 1 KiB destination inside a tile
     int Lp2;                // bytes per V^T row
 
-    // 16 wave-level loads: 8 for the K tile (2 rows each), 8 for the V^T tile (8 rows each)
+    // 8 wave-level loads: 4 for the K tile (2 rows each), 4 for the V^T tile (8 rows each)
     __device__ __forceinline__ void issue(uint8_t* stage, int key0) const {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, SFM_LDS(stage + lds0 + i * 4096), 16, kvoff[i & 1],
-                                                     (uint32_t)(key0 + 8 * i) * 512u, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, SFM_LDS(stage + lds0 + i * 8192), 16, kvoff,
+                                                     (uint32_t)(key0 + 16 * i) * 512u, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, SFM_LDS(stage + kKTile + lds0 + i * 4096), 16, vvoff,
-                                                     (uint32_t)(32 * i * Lp2 + key0 * 2), 0, 0);
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, SFM_LDS(stage + kKTile + lds0 + i * 8192), 16, vvoff,
+                                                     (uint32_t)(64 * i * Lp2 + key0 * 2), 0, 0);
     }
 };
 
@@ -81,7 +85,7 @@ __device__ __forceinline__ float col_max(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ o, int L, int Lp, int H, int nqb) {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kKTile];
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const uint16_t* Qh = q + (int64_t)bh * Lp * kD;
-    const int q0 = qb * kQB + wave * 32;
+    const int q0 = qb * kQB + wave * 16;
 
     Loader ld;
     ld.rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (int64_t)bh * Lp * kD), 0, Lp * kD * 2, kRsrcWord3);
@@ -106,23 +110,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ld.Lp2 = Lp * 2;
     ld.lds0 = (uint32_t)wave * 1024;
     {
-        // K tile: 1 KiB block (wave + 4i) holds rows r = 2(wave + 4i) + (lane >> 5) (relative to the
-        // tile), physical chunk lane & 31 = logical chunk ^ (r & 15); r & 15 depends on i only through
-        // 8 (i & 1)
-        for (int par = 0; par < 2; ++par) {
-            const int r = 2 * wave + 8 * par + (lane >> 5);
-            ld.kvoff[par] = (uint32_t)((r - 8 * par) * 512 + (((lane & 31) ^ (r & 15)) * 16));
+        // K tile: 1 KiB block (wave + 8i) holds rows r = 2 wave + (lane >> 5) + 16 i (relative to the
+        // tile), physical chunk lane & 31 = logical chunk ^ (r & 15), which does not depend on i
+        {
+            const int r = 2 * wave + (lane >> 5);
+            ld.kvoff = (uint32_t)(r * 512 + (((lane & 31) ^ (r & 15)) * 16));
         }
-        // V^T tile: 1 KiB block (wave + 4i) holds rows 8(wave + 4i) + (lane >> 3), physical chunk lane & 7
+        // V^T tile: 1 KiB block (wave + 8i) holds rows 8 wave + (lane >> 3) + 64 i, physical chunk lane & 7
         // = logical chunk ^ ((row >> 1) & 7) = logical ^ ((4 (wave & 1) + (lane >> 4)) & 7)
         const int vrow = 8 * wave + (lane >> 3);
         ld.vvoff = (uint32_t)(vrow * Lp * 2 + (((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) * 16));
     }
 
     // q fragments (B operand of S^T): rows q0 + qt*16 + lr, dims ks*32 + 8*lg .. +8
-    bf16x8 qf[2][8];
+    constexpr int NQT = 1;
+    bf16x8 qf[NQT][8];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             qf[qt][ks] = __builtin_bit_cast(
@@ -138,16 +142,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int vb0 = lr * 128 + csw + ((x >> 2) << 6);        // keys 0..31 of the tile
     const int vb1 = lr * 128 + csw + ((1 ^ (x >> 2)) << 6);  // keys 32..63
 
-    v4f oacc[2][16];
+    v4f oacc[NQT][16];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) oacc[qt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    float mrun[2] = {-1e30f, -1e30f};
+    float mrun[NQT];
+    for (int qt = 0; qt < NQT; ++qt) mrun[qt] = -1e30f;
     // row sums of P^T come from the matrix cores: a constant A fragment whose first row is all
     // ones (row 0 of the A operand lives in lanes 0, 16, 32, 48) turns O^T += V^T P^T into l += 1^T P^T, summing exactly the
     // fp16 weights that O accumulates; lane l (l < 16) holds query column l in lacc[qt][0]
-    v4f lacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    v4f lacc[NQT];
+    for (int qt = 0; qt < NQT; ++qt) lacc[qt] = v4f{0.f, 0.f, 0.f, 0.f};
     f16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (_Float16)(lr == 0 ? 1.0f : 0.0f);
@@ -157,9 +163,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const uint8_t* kl = stg;
         const uint8_t* vl = stg + kKTile;
         // S^T tile: s[qt][t4][r] = score(key = t4*16 + 4*lg + r, query = qt*16 + lr)
-        v4f s[2][4];
+        v4f s[NQT][4];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) s[qt][t4] = v4f{0.f, 0.f, 0.f, 0.f};
         bf16x8 kf[3][4];
@@ -169,6 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int t4 = 0; t4 < 4; ++t4)
                 kf[slot][t4] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + base + t4 * 8192));
         };
+        __builtin_amdgcn_s_setprio(1);
         load_kf(0, 0);
         load_kf(1, 1);
 #pragma unroll
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int qt = 0; qt < NQT; ++qt)
                     s[qt][t4] =
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -187,16 +194,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (key0 + t4 * 16 + 4 * lg + r >= L) {
-                        s[0][t4][r] = -INFINITY;
-                        s[1][t4][r] = -INFINITY;
-                    }
+                    if (key0 + t4 * 16 + 4 * lg + r >= L)
+#pragma unroll
+                        for (int qt = 0; qt < NQT; ++qt) s[qt][t4][r] = -INFINITY;
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // online softmax (exp2 domain), P^T packed as the B operand of O^T += V^T P^T
-        f16x8 pf[2][2];
+        f16x8 pf[NQT][2];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int qt = 0; qt < NQT; ++qt) {
             float mx = fmaxf(fmaxf(s[qt][0][0], s[qt][0][1]), fmaxf(s[qt][0][2], s[qt][0][3]));
 #pragma unroll
             for (int t4 = 1; t4 < 4; ++t4)
@@ -239,6 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 vf[slot][u] =
                     __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(vl + base + (4 * (g & 3) + u) * 2048));
         };
+        __builtin_amdgcn_s_setprio(1);
         load_vf(0, 0);
         load_vf(1, 1);
 #pragma unroll
@@ -249,13 +257,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int u = 0; u < 4; ++u) {
                 const int dt = 4 * (g & 3) + u;
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int qt = 0; qt < NQT; ++qt)
                     oacc[qt][dt] =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g % 3][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
             }
             if ((g & 3) == 3)
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
+                for (int qt = 0; qt < NQT; ++qt)
                     lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qt][h2], lacc[qt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // normalise and write o[b*L + query][h*256 + d]
     const int D = H * kD;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < NQT; ++qt) {
         const float l = __shfl(lacc[qt][0], lr, 64);
         const float inv = 1.0f / l;
         const int qi = q0 + qt * 16 + lr;
@@ -307,7 +315,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     if (L == 0) return hipSuccess;
     const int Lp = padded_len(L);
     const int nqb = Lp / kQB;
-    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(256), 0, st, q, k, vt, o, L, Lp, H, nqb);
+    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(512), 0, st, q, k, vt, o, L, Lp, H, nqb);
     return hipGetLastError();
 }
 
