@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--cpu-sample", default="block_1024", help="workload timed on the CPU oracle")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the dominant launch and a calibration copy (for rocprofv3 --pmc passes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the HBM traffic table and record from the FETCH_SIZE and WRITE_SIZE passes "
+                         "over --pmc-probe and exit (no GPU needed)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="print per-kernel tables (markdown) from a rocprofv3 --kernel-trace --stats output "
+                         "directory of this script and exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -192,6 +198,114 @@ def pmc_probe(sfm, synth, ctx, iters=10):
     print(json.dumps({"pmc_probe": "done", "copy_bytes": COPY_BYTES, "sources_sha256_16": sources_digest()}))
 
 
+def pmc_summary(fetch_dir, write_dir):
+    """Traffic of the dominant launch from two rocprofv3 --pmc passes over
+    --pmc-probe: each counter's mean per dispatch for the GEMM and for the copy of
+    COPY_BYTES, the copy fixing the counter's scale (true bytes / counted KiB)."""
+    import csv
+    import glob
+    M, K, F = ROOF_SHAPE
+    grid = (M // 256) * (2 * F // 256) * 256
+
+    def means(d, counter):
+        f = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+        if not f:
+            sys.exit(f"no counter_collection.csv under {d}")
+        g, c = [], []
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            if "gemm_fp8_kernel<256, 256, 2>" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
+                g.append(float(r["Counter_Value"]))
+            elif "copyBuffer" in r["Kernel_Name"]:
+                c.append(float(r["Counter_Value"]))
+        if not g or not c:
+            sys.exit(f"{counter}: no GEMM or copy dispatches in {d}")
+        return sum(g) / len(g), sum(c) / len(c), len(g)
+
+    fg, fc, n = means(fetch_dir, "FETCH_SIZE")
+    wg, wc, _ = means(write_dir, "WRITE_SIZE")
+    fs, ws = COPY_BYTES / (fc * 1024), COPY_BYTES / (wc * 1024)
+    fb, wb = fg * 1024 * fs, wg * 1024 * ws
+    alg = M * K + 2 * F * K + 2 * F * 4 + M * 4 + M * F * 2
+    print(f"| counter (KiB per dispatch, mean of {n}) | GEMM | copy of {COPY_BYTES // 1024} KiB | scale |")
+    print("|---|---|---|---|")
+    print(f"| FETCH_SIZE | {fg:.1f} | {fc:.1f} | {fs:.4f} |")
+    print(f"| WRITE_SIZE | {wg:.1f} | {wc:.1f} | {ws:.4f} |")
+    print()
+    print(f"Scaled: fetch {fb / 1e6:.1f} MB + write {wb / 1e6:.1f} MB = **{(fb + wb) / 1e6:.1f} MB per launch**.")
+    print(f"Algorithmic bytes (A codes + weights + scales + bf16 output): {alg / 1e6:.1f} MB.")
+    print()
+    rec = {"kernel": "gemm_fp8_kernel<256, 256, SWIGLU>", "shape": f"M {M} N {2 * F} K {K}",
+           "bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4), "sources_sha256_16": sources_digest()}
+    print("traffic-record: " + json.dumps(rec))
+
+
+def trace_summary(out_dir, layers=34):
+    """Markdown tables from rocprofv3's kernel_trace.csv / kernel_stats.csv under
+    out_dir: every launch of this library's kernels grouped by (kernel, grid in
+    workgroups), and the dominant launch (SwiGLU gate/up at the conditional grid)
+    averaged over its last `layers` launches, which are those of the last step
+    (the one bench times with events when run as bench.py --steps K)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def short(n):
+        n = n.replace("sfm::(anonymous namespace)::", "").replace("sfm::", "")
+        n = n[5:] if n.startswith("void ") else n
+        depth, cut = 0, len(n)
+        for i, ch in enumerate(n):      # drop the argument list, keep template arguments
+            if ch == "<":
+                depth += 1
+            elif ch == ">":
+                depth -= 1
+            elif ch == "(" and depth == 0:
+                cut = i
+                break
+        return n[:cut]
+
+    trace = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not trace:
+        sys.exit(f"no kernel_trace.csv under {out_dir}")
+    groups = defaultdict(list)
+    dominant = []
+    rows = sorted(csv.DictReader(open(trace[0])), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        if "sfm::" not in r["Kernel_Name"]:
+            continue
+        wg = 1
+        for ax in "XYZ":
+            wg *= int(r[f"Grid_Size_{ax}"]) // max(int(r[f"Workgroup_Size_{ax}"]), 1)
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        name = short(r["Kernel_Name"])
+        groups[(name, wg)].append(us)
+        M, _, F = ROOF_SHAPE
+        if name == "gemm_fp8_kernel<256, 256, 2>" and wg == (M // 256) * (2 * F // 256):
+            dominant.append(us)
+    total = sum(sum(v) for v in groups.values())
+    print("| kernel | workgroups | launches | avg us | share of GPU time (%) |")
+    print("|---|---|---|---|---|")
+    for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{name}` | {wg} | {len(v)} | {sum(v) / len(v):.1f} | {100 * sum(v) / total:.1f} |")
+    if dominant:
+        last = dominant[-layers:]
+        print()
+        print(f"Dominant launch `gemm_fp8_kernel<256, 256, 2>` at {(ROOF_SHAPE[0] // 256) * (2 * ROOF_SHAPE[2] // 256)} "
+              f"workgroups: {len(dominant)} launches, average {sum(dominant) / len(dominant):.2f} us; "
+              f"last {len(last)} (the last step): average {sum(last) / len(last):.2f} us.")
+    stats = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True))
+    if stats:
+        print()
+        print("| kernel (rocprofv3 --stats) | calls | avg us | % |")
+        print("|---|---|---|---|")
+        for r in csv.DictReader(open(stats[0])):
+            if "sfm::" in r["Name"]:
+                print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                      f"{float(r['Percentage']):.2f} |")
+
+
 def cpu_baseline(sample):
     """The CPU oracle (float64 NumPy) on one full-width block of the step's
     conditional shape: 4608 tokens through one block.  Scaled to block tokens/s."""
@@ -220,6 +334,12 @@ def cpu_baseline(sample):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
