@@ -214,6 +214,140 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
     }
 }
 
+// Epilogue of a wave's TM x TN tile of 32x32 accumulators (TM = 32 FM,
+// TN = 32 FN) computed with the weight fragment as the MFMA's first operand,
+// so that acc[i][j] holds the transposed block: element r of acc[i][j] in lane
+// l is tile row 32 i + (l & 31) and B-tile column 32 j + 8 (r >> 2) + 4 (l >> 5)
+// + (r & 3).  A lane thus owns one row per i and four consecutive columns per
+// (j, r >> 2): one row scale per i, the column scales four at a time, and one
+// 8-byte (bf16) or 16-byte (fp32) LDS write per four values.  The tile is
+// staged through the wave's own LDS region and read back in 16-byte row chunks
+// for the global stores, as in gemm_epilogue_lds.
+//   STORE / SWIGLU: bf16 rows of OC = TN (TN / 2) columns, 16-byte chunk c of
+//     row r at physical chunk c ^ s(r) (s spreads the 32 rows of a write over
+//     the banks).
+//   RESID_GATE: gate * y staged in fp32, TM / 2 rows per pass, rows padded by one
+//     chunk when TN / 4 chunks are not a multiple of 16 (else XOR-swizzled);
+//     the pass's residual chunks are loaded before its staging writes, so their
+//     latency overlaps them, then added on the way out (one bf16 rounding).
+// Scales come from LDS, where the kernel put them before its main loop: rsl
+// = row scales of the wave's rows, csl = scales of the wave's B-tile columns,
+// gl = gate rows of batches bt0, bt0 + 1, bt0 + 2 (stride BN floats, offset to
+// the wave's columns; RESID only).  The gate row of token row m is batch m / L
+// and a wave's rows touch at most two batches (L >= TM).  lds: the wave's
+// staging region (at least TM * TN * 2 bytes; the RESID padding needs
+// TM / 2 * (TN * 4 + 16)).
+template <int EPI, int BN, int TN, int FM, int FN>
+__device__ __forceinline__ void gemm_epilogue_lds_t(const v16f (&acc)[FM][FN], uint8_t* lds, int m0w, int wn, int tn,
+                                                    int lane, int M, int N, int L, uint16_t* out,
+                                                    const uint16_t* resid, const float* rsl, const float* csl,
+                                                    const float* gl, int bt0) {
+    constexpr int TM = 32 * FM;
+    const int lc = lane & 31, lg = lane >> 5;
+    float rs[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) rs[i] = rsl[32 * i + lc];
+    auto colscale = [&](int c) { return *reinterpret_cast<const v4f*>(csl + c); };
+
+    if constexpr (EPI == SFM_EPI_STORE || EPI == SFM_EPI_SWIGLU) {
+        constexpr bool SW = EPI == SFM_EPI_SWIGLU;
+        constexpr int OC = SW ? TN / 2 : TN;  // output columns of the wave tile
+        constexpr int NCH = OC / 8;           // 16-byte chunks per LDS row
+        static_assert(NCH == 4 || NCH == 8 || NCH == 16, "row swizzle");
+        // rows 16 / NCH apart share a bank line; XOR-ing their chunks by the row's line index
+        // puts 16 consecutive rows on 16 distinct 16-byte bank slots
+        auto swz = [](int ch, int row) { return ch ^ ((row / (16 / NCH)) & (NCH - 1)); };
+        const int64_t ld_out = SW ? N / 2 : N;
+        const int64_t col0 = SW ? (int64_t)tn * (BN / 2) + wn * (TN / 2) : (int64_t)tn * BN + wn * TN;
+#pragma unroll
+        for (int j = 0; j < (SW ? FN / 2 : FN); ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = 32 * j + 8 * q + 4 * lg;
+                const v4f cg = colscale(c);
+                const v4f cu = SW ? colscale(c + TN / 2) : cg;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (SW)
+                            y[e] = swiglu_fast(acc[i][j][4 * q + e] * rs[i] * cg[e],
+                                               acc[i][j + FN / 2][4 * q + e] * rs[i] * cu[e]);
+                        else
+                            y[e] = acc[i][j][4 * q + e] * rs[i] * cg[e];
+                    }
+                    const int row = 32 * i + lc;
+                    *reinterpret_cast<uint2*>(lds + row * (OC * 2) + (swz(c >> 3, row) << 4) + lg * 8) =
+                        make_uint2(cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]));
+                }
+            }
+        }
+        // read back: chunk q of the tile is row q / NCH, chunk q % NCH
+#pragma unroll
+        for (int s = 0; s < TM * NCH / 64; ++s) {
+            const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (OC * 2) + (swz(ch, row) << 4));
+            const int grow = m0w + row;
+            if (grow < M) *reinterpret_cast<uint4*>(out + (int64_t)grow * ld_out + col0 + ch * 8) = v;
+        }
+    } else {
+        constexpr int NCH = TN / 4;                   // 16-byte chunks (four fp32) per row
+        constexpr bool PAD = NCH % 16 != 0;
+        constexpr int PITCH = TN * 4 + (PAD ? 16 : 0);
+        auto swz = [](int ch, int row) { return PAD ? ch : ch ^ (row & 15); };
+        constexpr int PR = TM / 2;                    // rows per pass
+        constexpr int NS = PR * NCH / 64;             // chunks per lane per pass
+        static_assert(PR * NCH % 64 == 0, "whole chunks per lane");
+        const int64_t col0 = (int64_t)tn * BN + wn * TN;
+        const int r_first = min(m0w, M - 1), r_last = min(m0w + TM - 1, M - 1);
+        const int b_first = r_first / L, b_last = r_last / L;
+        const int row_split = (b_first + 1) * L;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            // residual chunks of this pass first: their latency overlaps the staging writes
+            uint2 rv[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
+                const int grow = min(m0w + PR * p + row, M - 1);
+                rv[s] = *reinterpret_cast<const uint2*>(resid + (int64_t)grow * N + col0 + ch * 4);
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 32 * j + 8 * q + 4 * lg;
+                    const v4f cs = colscale(c);
+                    const v4f g0 = *reinterpret_cast<const v4f*>(gl + (b_first - bt0) * BN + c);
+                    const v4f g1 = *reinterpret_cast<const v4f*>(gl + (b_last - bt0) * BN + c);
+#pragma unroll
+                    for (int ii = 0; ii < FM / 2; ++ii) {
+                        const int i = p * (FM / 2) + ii;
+                        const int row = 32 * ii + lc;  // row inside the pass
+                        const v4f g = m0w + 32 * i + lc < row_split ? g0 : g1;
+                        v4f v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = g[e] * (acc[i][j][4 * q + e] * rs[i] * cs[e]);
+                        *reinterpret_cast<v4f*>(lds + row * PITCH + (swz(c >> 2, row) << 4)) = v;
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
+                const v4f v = *reinterpret_cast<const v4f*>(lds + row * PITCH + (swz(ch, row) << 4));
+                const int grow = m0w + PR * p + row;
+                uint2 pk;
+                pk.x = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].x) + v[0], bf16_to_f32((uint16_t)(rv[s].x >> 16)) + v[1]);
+                pk.y = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].y) + v[2], bf16_to_f32((uint16_t)(rv[s].y >> 16)) + v[3]);
+                if (grow < M) *reinterpret_cast<uint2*>(out + (int64_t)grow * N + col0 + ch * 4) = pk;
+            }
+        }
+    }
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
 // XCD b % 8); renumber so that each XCD gets one contiguous range of ids and
 // the tiles it works on at the same time share its L2.

@@ -81,6 +81,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int NQ = (FM / 2) * FN;          // MFMAs per quarter-stage
     constexpr int STAGE = (BM + BN) * kBK;
     static_assert(FM % 2 == 0, "quarter-stages split the row tiles in two");
+    // each wave stages its epilogue in a quarter of the ring
+    static_assert((EPI == SFM_EPI_RESID_GATE ? TM / 2 * (TN * 4 + ((TN / 4) % 16 ? 16 : 0))
+                                             : TM * (EPI == SFM_EPI_SWIGLU ? TN / 2 : TN) * 2) <= STAGE / 2,
+                  "epilogue staging fits the wave's quarter of the ring");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     auto mfma = [&](int set, int q, int i0) {
         const int i = i0 + q / FN, j = q % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][FN + i], fr[set][j], acc[i][j], 0, 0, 0,
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][j], fr[set][FN + i], acc[i][j], 0, 0, 0,
                                                                     0, 0, 0);
     };
     // quarter-stage: NQ MFMAs on fragment set `set`, row tiles i0 .. i0 + FM/2, with the
@@ -161,6 +165,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
+    // the epilogue's scales go to LDS behind the ring: row scales [BM], column scales [BN] and,
+    // for the gated residual, the gate rows of the (at most three) batches the tile's rows touch
+    // [3][BN]; their loads are issued before the first stages' and land under them
+    constexpr int NSC = BM + (EPI == SFM_EPI_RESID_GATE ? 4 : 1) * BN;
+    constexpr int NSL = (NSC + 255) / 256;
+    float* scl = reinterpret_cast<float*>(smem + 2 * STAGE);
+    const int bt0 = EPI == SFM_EPI_RESID_GATE ? min(m0, M - 1) / L : 0;
+    float scv[NSL];
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) {
+        const int e = tid + 256 * k;
+        float v = 1.0f;
+        if (e < BM) {
+            if (sa) v = sa[min(m0 + e, M - 1)];
+        } else if (e < BM + BN) {
+            if (sw) v = sw[weight_row<EPI, BN, TN>(e - BM, tn, N)];
+        } else if (e < NSC) {
+            const int g = (e - BM - BN) / BN, c = (e - BM - BN) % BN;
+            v = gate[(int64_t)min(bt0 + g, (M - 1) / L) * gate_stride + (int64_t)tn * BN + c];
+        }
+        scv[k] = v;
+    }
+
     // K % 256 == 0 (checked by the caller): nks >= 2 and even
     const int nks = K / kBK;
 #pragma unroll
@@ -168,6 +195,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int v = 0; v < NV; ++v) vmem(v, smem + STAGE, ra, rb, kBK);
     wait_vm_lgkm0<NV>();
+#pragma unroll
+    for (int k = 0; k < NSL; ++k)
+        if (tid + 256 * k < NSC) scl[tid + 256 * k] = scv[k];
     lds_barrier();
 #pragma unroll
     for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
@@ -199,8 +229,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the ring is free once every wave is past its last read: each wave then stages its
     // epilogue in its own quarter of the LDS
     lds_barrier();
-    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
-                                           resid, gate, gate_stride, sa, sw);
+    gemm_epilogue_lds_t<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
+                                             resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
 }
 
 template <int BM, int BN, int EPI>
@@ -209,7 +239,8 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = (size_t)2 * (BM + BN) * kBK;
+    // two ring stages, then the epilogue's scales (row, column and three gate rows)
+    const size_t shm = (size_t)2 * (BM + BN) * kBK + (size_t)(BM + 4 * BN) * 4;
     auto kern = gemm_fp8_kernel<BM, BN, EPI>;
     static bool attr_set = false;
     if (!attr_set) {
