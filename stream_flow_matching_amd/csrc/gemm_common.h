@@ -24,50 +24,6 @@ __device__ __forceinline__ int64_t weight_row(int j, int tn, int N) {
     }
 }
 
-// Epilogue over a wave's FM x FN grid of 16x16 accumulators.  Accumulator
-// acc[i][j][r] of lane l is output row m0w + 16 i + 4 (l >> 4) + r and B-tile
-// row n0w + 16 j + (l & 15).  row_scale(row) and col_scale(weight row) give the
-// dequantisation factors (1 for bf16 operands).
-template <int EPI, int BN, int TN, int FM, int FN, typename RowScale, typename ColScale>
-__device__ __forceinline__ void gemm_epilogue(const v4f (&acc)[FM][FN], int m0w, int wn, int tn, int lane, int M,
-                                              int N, int L, uint16_t* out, const uint16_t* resid, const float* gate,
-                                              int64_t gate_stride, RowScale row_scale, ColScale col_scale) {
-    const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0w + i * 16 + 4 * lg + r;
-            if (row >= M) continue;
-            const float s_a = row_scale(row);
-            if constexpr (EPI == SFM_EPI_SWIGLU) {
-                const int F = N / 2;
-#pragma unroll
-                for (int j = 0; j < FN / 2; ++j) {
-                    const int64_t col = (int64_t)tn * (BN / 2) + wn * (TN / 2) + j * 16 + lr;
-                    const float g = acc[i][j][r] * s_a * col_scale(col);
-                    const float u = acc[i][j + FN / 2][r] * s_a * col_scale(F + col);
-                    const float sg = g / (1.0f + expf(-g));
-                    out[(int64_t)row * F + col] = f32_to_bf16(sg * u);
-                }
-            } else {
-                const int b = row / L;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int64_t col = (int64_t)tn * BN + wn * TN + j * 16 + lr;
-                    const float y = acc[i][j][r] * s_a * col_scale(col);
-                    if constexpr (EPI == SFM_EPI_STORE) {
-                        out[(int64_t)row * N + col] = f32_to_bf16(y);
-                    } else {
-                        const float xr = bf16_to_f32(resid[(int64_t)row * N + col]);
-                        out[(int64_t)row * N + col] = f32_to_bf16(xr + gate[(int64_t)b * gate_stride + col] * y);
-                    }
-                }
-            }
-        }
-    }
-}
-
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -26,8 +26,13 @@
 // LDS banks.  Rows past M are clamped to row M - 1 for loading (their results
 // are never stored).  MFMA operands: lane l holds row (l & 31) and the same
 // 32-byte k-slice (l >> 5) of A and W, so the product does not depend on how
-// the instruction orders k inside a lane.  Tiles are numbered XCD by XCD and,
-// in each XCD's range, in 8-row groups (L2 reuse of both operands).
+// the instruction orders k inside a lane.  The weight fragment is the first
+// operand, so each accumulator block is transposed: a lane owns four
+// consecutive output columns of one row, which the epilogue scales and stages
+// through LDS in 8- or 16-byte pieces.  The row and column scales (and the gate
+// rows of the gated residual) are loaded into LDS behind the ring at the start,
+// under the first stages' loads.  Tiles are numbered XCD by XCD and, in each
+// XCD's range, in 8-row groups (L2 reuse of both operands).
 #include "gemm_common.h"
 
 namespace sfm {
