@@ -237,6 +237,35 @@ def test_linear_fp8_gated_residual_full_width(sfm, ctx_full, M):
     assert rel_l2(got - np64(resid[rows]), ref - np64(resid[rows])) < 1e-2
 
 
+@pytest.mark.parametrize("M,Nw,inplace", [(4352, 4608, True), (18432, 4096, False)])
+def test_linear_fp8_gated_residual_three_batches_per_tile(sfm, ctx_full, M, Nw, inplace):
+    """Gated residual with short batches (L 136): the launcher picks 256-row
+    tiles (256 x 192 at N 4608, 256 x 256 at N 4096 and M 18432), so one tile's
+    rows touch three batches and each wave two; sampled rows around batch and
+    tile boundaries against the oracle."""
+    _say("linear fp8 resid 3 batches", M, Nw)
+    K, L = 256, 136
+    a = _rand_codes((M, K), ("l3", M))
+    sa = (torch.rand(M, generator=torch.Generator().manual_seed(5)) * 2e-3 + 1e-3).float()
+    wq, ws = synth.fp8_weight(Nw, K, ("l3w", Nw))
+    keep = (wq.to(DEV), ws.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    resid = synth.bf16_normal((M, Nw), ("l3r", M), 1.0)
+    gate = synth.randn(((M + L - 1) // L, Nw), ("l3g", M), 0.5)
+    x = resid.to(DEV)
+    out = x if inplace else torch.empty_like(x)
+    sfm.sfm_linear(ctx_full, 1, a.to(DEV), sa.to(DEV), w, out, x, gate.to(DEV), Nw, M=M, L=L)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 127, 128, 135, 136, 255, 256, 271, 272, 383, 384, 407, 408, 511, 512,
+                            2 * 4096 // 3, M // 2, M - 137, M - 136, M - 1}))
+    y = (N.e4m3_decode(npu8(a[rows])) @ N.e4m3_decode(npu8(wq)).T) * sa.numpy()[rows, None].astype(np.float64) \
+        * ws.numpy()[None, :].astype(np.float64)
+    ref = N.bf16_round(np64(resid[rows]) + np64(gate)[rows // L] * y)
+    got = np64(out[rows])
+    assert rel_l2(got, ref) < 2e-3
+    assert rel_l2(got - np64(resid[rows]), ref - np64(resid[rows])) < 1e-2
+
+
 # --------------------------------------------------------------------------- a12 NF4 linear
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
