@@ -17,6 +17,7 @@ FP8-E4M3 / NF4 weight codes).  Citations name the source page and its section:
   [Deploy]   "Ideogram 4.0 free local deployment" blog post (post.smzdm.com),
              section 1.3 (asymmetric CFG, scale 4.0), section 2 (FP8 E4M3
              original weights) and section 2.1 (NF4, block size 64, QLoRA).
+  [Note]     also section "Infra" (sampling presets) for the sampler.
   [Tuner]    SimpleTuner Ideogram 4 quick-start, sections "Text embed cache"
              (4608-d projected text features) and "Validation" (separate
              image-only unconditional transformer).
@@ -42,9 +43,14 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
   model_velocity         zero-layer reduction to the final layer of the embedding
   euler_cfg, cfg_step    closed forms; uncond ignores text; guidance 1 gives cond
   param_count            the ~9.3B of the spec table
+  sampler.time_grid      endpoints, order, closed-form median sigmoid(log 2) = 2/3,
+                         symmetry without shift, scipy's normal quantile
+  sampler presets        the research note's preset table (tests/golden)
+  sampler.euler_loop / sample   constant velocity telescopes to z + v, the linear
+                         ODE's product form, chaining of the guided steps
 Parity unpinned: the whole model against a real checkpoint (none exists here);
 the modulation chunk order, the timestep MLP and the final layer are readings
 of prose, pinned only structurally.
 """
 
-from . import numerics, dit  # noqa: F401
+from . import numerics, dit, sampler  # noqa: F401
