@@ -6,7 +6,9 @@ Prints ONE JSON line.  `value` is DiT block tokens/s over the whole step
 (34 * (4608 + 4096) block-token passes per step).  The step's TFLOP/s and
 fraction of the FP8 matrix peak, the single-block figures at the other
 workload shapes, the roofline of the dominant kernel (the FP8 gate/up SwiGLU
-projection) and the CPU oracle baseline are reported beside it.
+projection) and the CPU oracle baseline are reported beside it, and so is the
+time of one whole 1024x1024 image with the V4_TURBO_12 and V4_QUALITY_48
+sampler presets (12 / 48 guided steps; outside the timed steps).
 
 Inputs are synthetic and seeded (weights FP8 E4M3 from N(0, 0.02), latent and
 text N(0, 1), t from the logit-normal draw); all of them are resident in HBM
@@ -69,7 +71,7 @@ def time_gpu(fn, iters, warmup=1):
     return s.elapsed_time(e) / iters / 1e3   # seconds per call
 
 
-def cfg_step_bench(sfm, synth, ctx, steps, warmup):
+def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
     """Times `steps` CFG steps between two synchronisations; the last timed step
     also records HIP events around each of its gate/up projection launches
     (sfm_cfg_step_timed), which gives that kernel's launch durations inside the
@@ -102,9 +104,20 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup):
     sec = (time.perf_counter() - t0) / steps
     launches = [evb[i].elapsed_time(eve[i]) * 1e3 for i in range(rec)]   # microseconds
     ok = bool(torch.isfinite(zo).all())
+    # whole images with the sampler presets (outside the timed steps above)
+    samples = {}
+    for name, pid in presets:
+        t_grid, g = sfm.sfm_preset_schedule(pid, 16 * w.gh, 16 * w.gw)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sfm.sfm_sample(ctx, cm, um, text, z, zo, t_grid, g, w.B, w.T, w.gh, w.gw, ws)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        samples[name] = {"steps": len(g), "s_per_image": round(el, 4), "ms_per_step": round(el / len(g) * 1e3, 3),
+                         "finite": bool(torch.isfinite(zo).all())}
     del cond, unc, cm, um, ws
     torch.cuda.empty_cache()
-    return sec, ok, launches[:w.layers], launches[w.layers:]
+    return sec, ok, launches[:w.layers], launches[w.layers:], samples
 
 
 def block_bench(sfm, synth, ctx, name, iters=5):
@@ -356,7 +369,9 @@ def main():
         return
 
     w = synth.WORKLOADS["cfg_step_1024"]
-    sec, ok, gu_cond, gu_uncond = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup)
+    presets = () if args.no_extra else (("V4_TURBO_12", sfm.SFM_PRESET_V4_TURBO_12),
+                                         ("V4_QUALITY_48", sfm.SFM_PRESET_V4_QUALITY_48))
+    sec, ok, gu_cond, gu_uncond, samples = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup, presets)
     tokens = w.layers * (w.B * (w.T + w.gh * w.gw) + w.B * w.gh * w.gw)
     flops = w.layers * (block_flops(w.T + w.gh * w.gw, w.B) + block_flops(w.gh * w.gw, w.B))
     step_tflops = flops / sec / 1e12
@@ -390,6 +405,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "blocks": extra,
+        "sampler_1024": samples,
     }
     print(json.dumps(line))
 

@@ -279,6 +279,51 @@ int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, co
                        int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
                        void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded);
 
+/* ---------------------------------------------------------------- sampler */
+
+/* Time grid of the logit-normal schedule (research note, "Training method":
+ * logit-normal noise schedule with parameters (mu, std), mu shifted by
+ * 0.5 * ln(num_pixels / 512^2) with the image size).  Writes n_steps + 1 host
+ * doubles t_out[i] = sigmoid(mu' + std * Phi^-1(1 - i / n_steps)): t_out[0] = 1
+ * (noise), t_out[n_steps] = 0 (clean), strictly decreasing (the quantiles of
+ * the shifted distribution at evenly spaced probabilities; the pages name the
+ * distribution, not the grid).  Host only.  SFM_E_INVALID_ARG for n_steps < 1,
+ * NULL t_out, num_pixels < 1, non-finite mu / std or std <= 0. */
+int sfm_time_grid(int n_steps, double mu, double std_dev, int64_t num_pixels, double* t_out);
+
+/* Presets of the research note, "Infra": steps, the number at the main
+ * guidance weight (the rest are polish steps at the lower weight), and the
+ * schedule's (mu, std). */
+enum {
+    SFM_PRESET_V4_QUALITY_48 = 0, /* 48 steps: 45 at 7, 3 at 3; mu 0.0, std 1.5 */
+    SFM_PRESET_V4_DEFAULT_20 = 1, /* 20 steps: 18 at 7, 2 at 3; mu 0.0, std 1.75 */
+    SFM_PRESET_V4_TURBO_12 = 2    /* 12 steps: 11 at 7, 1 at 3; mu 0.5, std 1.75 */
+};
+typedef struct sfm_preset_info {
+    int32_t n_steps, n_main;
+    float guidance_main, guidance_polish;
+    double mu, std_dev;
+} sfm_preset_info;
+int sfm_preset(int preset, sfm_preset_info* out);
+
+/* A preset at an image size: t_out[0 .. n] (sfm_time_grid with the preset's
+ * mu / std and height_px * width_px pixels) and guidance_out[0 .. n - 1]
+ * (main weight, then the polish weight), both host arrays with room for
+ * `capacity` >= n steps.  Returns n > 0, or a negative SFM_E_* status. */
+int sfm_preset_schedule(int preset, int height_px, int width_px, double* t_out, float* guidance_out, int capacity);
+
+/* n_steps guided Euler steps (research note, "Training method": Euler
+ * integration z_{t - dt} = z_t + v dt with a per-step guidance weight): step i
+ * is sfm_cfg_step at t = (float)t[i], dt = (float)(t[i] - t[i + 1]), guidance
+ * guidance[i], reading z for the first step and z_out afterwards (z_out may
+ * equal z).  t (n_steps + 1) and guidance (n_steps) are host arrays; t must be
+ * finite and strictly decreasing.  Workspace: sfm_step_workspace_bytes.  All
+ * checks run before the first step is enqueued; errors as sfm_cfg_step plus
+ * SFM_E_INVALID_ARG for the arrays. */
+int sfm_sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+               const uint16_t* text, const float* z, float* z_out, const double* t, const float* guidance,
+               int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- errors */
 const char* sfm_status_string(int status);
 const char* sfm_last_error(void);

@@ -15,10 +15,10 @@
 using namespace sfm;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int sfm::fail(int code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -27,6 +27,8 @@ int fail(int code, const char* fmt, ...) {
     g_err = buf;
     return code;
 }
+
+namespace {
 
 #define SFM_TRY_HIP(expr)                                                                           \
     do {                                                                                            \

@@ -125,6 +125,9 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int padded_len(int L) { return (int)round_up(L, 128); }
 
+// Records a printf-style message for sfm_last_error (thread-local) and returns code.
+int fail(int code, const char* fmt, ...);
+
 // ------------------------------------------------------------------ launchers
 // All launchers enqueue on `st` and return hipError_t of the launch.
 

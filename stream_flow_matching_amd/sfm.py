@@ -49,6 +49,16 @@ class sfm_block_weights(ctypes.Structure):
                 ("mod_b", ctypes.c_void_p)]
 
 
+class sfm_preset_info(ctypes.Structure):
+    _fields_ = [("n_steps", ctypes.c_int32), ("n_main", ctypes.c_int32), ("guidance_main", ctypes.c_float),
+                ("guidance_polish", ctypes.c_float), ("mu", ctypes.c_double), ("std_dev", ctypes.c_double)]
+
+
+SFM_PRESET_V4_QUALITY_48 = 0
+SFM_PRESET_V4_DEFAULT_20 = 1
+SFM_PRESET_V4_TURBO_12 = 2
+
+
 class sfm_model_weights(ctypes.Structure):
     _fields_ = [("num_layers", ctypes.c_int32), ("blocks", ctypes.POINTER(sfm_block_weights)),
                 ("x_w", ctypes.c_void_p), ("x_b", ctypes.c_void_p), ("t_w1", ctypes.c_void_p),
@@ -91,6 +101,11 @@ SIGNATURES = {
     "sfm_cfg_step_timed": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
                                 _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P),
                                 ctypes.POINTER(_P), _I, ctypes.POINTER(_I)]),
+    "sfm_time_grid": (_I, [_I, ctypes.c_double, ctypes.c_double, _I64, _P]),
+    "sfm_preset": (_I, [_I, ctypes.POINTER(sfm_preset_info)]),
+    "sfm_preset_schedule": (_I, [_I, _I, _I, _P, _P, _I]),
+    "sfm_sample": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P, _P,
+                        _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "sfm_status_string": (ctypes.c_char_p, [_I]),
     "sfm_last_error": (ctypes.c_char_p, []),
 }
@@ -283,6 +298,46 @@ def sfm_cfg_step_timed(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z
                                     float(guidance), B, T, gh, gw, _ptr(v_c_out), _ptr(v_u_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream), b, e, n, ctypes.byref(rec)))
     return rec.value
+
+
+def sfm_time_grid(n_steps, mu, std_dev, num_pixels):
+    """Host time grid (n_steps + 1 float64 values, 1 -> 0) as a numpy array."""
+    import numpy as np
+    t = np.zeros(max(int(n_steps), 0) + 1, np.float64)
+    _check(lib().sfm_time_grid(int(n_steps), float(mu), float(std_dev), int(num_pixels), t.ctypes.data_as(_P)))
+    return t
+
+
+def sfm_preset(preset):
+    info = sfm_preset_info()
+    _check(lib().sfm_preset(int(preset), ctypes.byref(info)))
+    return info
+
+
+def sfm_preset_schedule(preset, height_px, width_px, capacity=64):
+    """(t grid, guidance weights) of a preset at an image size, as numpy arrays."""
+    import numpy as np
+    t = np.zeros(capacity + 1, np.float64)
+    g = np.zeros(capacity, np.float32)
+    n = lib().sfm_preset_schedule(int(preset), int(height_px), int(width_px), t.ctypes.data_as(_P),
+                                  g.ctypes.data_as(_P), int(capacity))
+    _check(min(n, 0))
+    return t[:n + 1].copy(), g[:n].copy()
+
+
+def sfm_sample(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, t, guidance, B, T, gh, gw, ws,
+               stream=None):
+    """len(guidance) guided Euler steps over the host grid t (len(guidance) + 1
+    decreasing values)."""
+    import numpy as np
+    t = np.ascontiguousarray(t, np.float64)
+    g = np.ascontiguousarray(guidance, np.float32)
+    n = len(g)
+    if len(t) != n + 1:
+        raise ValueError("t needs one more value than guidance")
+    _check(lib().sfm_sample(ctx.handle, ctypes.byref(cond.c), ctypes.byref(uncond.c), _ptr(text) if T > 0 else None,
+                            _ptr(z), _ptr(z_out), t.ctypes.data_as(_P), g.ctypes.data_as(_P), n, B, T, gh, gw,
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def workspace(nbytes, device="cuda"):

@@ -135,3 +135,52 @@ def test_context_creation_without_a_gpu_fails_cleanly(S):
     h = ctypes.c_void_p()
     st = S.lib().sfm_context_create(ctypes.byref(d), 0, ctypes.byref(h))
     assert st in (-4, -6, -1) and not h.value
+
+
+# --------------------------------------------------------------------------- sampler (host functions)
+
+@pytest.mark.parametrize("n,mu,std,px", [(48, 0.0, 1.5, 1024 * 1024), (20, 0.0, 1.75, 512 * 512),
+                                          (12, 0.5, 1.75, 2048 * 352), (1, 0.0, 1.0, 256 * 256),
+                                          (7, -1.25, 0.5, 1536 * 640)])
+def test_time_grid_matches_the_oracle(S, n, mu, std, px):
+    from oracle import sampler as O
+    t = S.sfm_time_grid(n, mu, std, px)
+    ref = np.array(O.time_grid(n, mu, std, px))
+    assert t[0] == 1.0 and t[-1] == 0.0
+    assert np.max(np.abs(t - ref)) < 1e-14
+
+
+@pytest.mark.parametrize("preset,name", [(0, "V4_QUALITY_48"), (1, "V4_DEFAULT_20"), (2, "V4_TURBO_12")])
+def test_presets_match_the_oracle(S, preset, name):
+    from oracle import sampler as O
+    n, n_main, g_main, g_pol, mu, std = O.PRESETS[name]
+    info = S.sfm_preset(preset)
+    assert (info.n_steps, info.n_main, info.guidance_main, info.guidance_polish, info.mu, info.std_dev) == \
+        (n, n_main, g_main, g_pol, mu, std)
+    t, g = S.sfm_preset_schedule(preset, 1024, 768)
+    rt, rg = O.preset_grid(name, 1024, 768)
+    assert np.max(np.abs(t - np.array(rt))) < 1e-14
+    assert list(g) == rg
+
+
+def test_sampler_argument_checks(S):
+    L = S.lib()
+    P = ctypes.c_void_p
+    t = np.zeros(4)
+    assert L.sfm_time_grid(0, 0.0, 1.0, 100, t.ctypes.data_as(P)) == -1
+    assert L.sfm_time_grid(3, 0.0, 0.0, 100, t.ctypes.data_as(P)) == -1
+    assert L.sfm_time_grid(3, float("nan"), 1.0, 100, t.ctypes.data_as(P)) == -1
+    assert L.sfm_time_grid(3, 0.0, 1.0, 0, t.ctypes.data_as(P)) == -1
+    assert L.sfm_time_grid(3, 0.0, 1.0, 100, None) == -1
+    assert L.sfm_preset(3, None) == -1
+    g = np.zeros(4, np.float32)
+    assert L.sfm_preset_schedule(2, 1024, 1024, t.ctypes.data_as(P), g.ctypes.data_as(P), 4) == -1   # capacity
+    good = P(1 << 20)
+    tt = np.array([1.0, 0.5, 0.5, 0.0])      # not strictly decreasing
+    gg = np.full(3, 4.0, np.float32)
+    assert L.sfm_sample(None, None, None, None, good, good, tt.ctypes.data_as(P), gg.ctypes.data_as(P), 3, 1, 0,
+                        16, 16, good, 0, None) == -1
+    assert L.sfm_sample(None, None, None, None, good, good, None, gg.ctypes.data_as(P), 3, 1, 0, 16, 16, good, 0,
+                        None) == -1
+    assert L.sfm_sample(None, None, None, None, good, good, tt.ctypes.data_as(P), gg.ctypes.data_as(P), 0, 1, 0,
+                        16, 16, good, 0, None) == -1

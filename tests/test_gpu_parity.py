@@ -570,6 +570,35 @@ def test_cfg_step_timed_matches_untimed(sfm, ctx_tiny):
     assert all(evs[i].elapsed_time(evs[6 + i]) > 0 for i in range(4))
 
 
+def test_sample_tiny_against_oracle_sampler(sfm, ctx_tiny):
+    """Four guided Euler steps over the logit-normal grid (V4 polish tail: the
+    last step at the lower weight) with 3-layer tiny models: the latent's change
+    against the oracle sampler, and the same result as chaining sfm_cfg_step by
+    hand (bitwise)."""
+    from oracle import sampler as OS
+    _say("sample tiny")
+    w = synth.Workload("tiny_sample", synth.TINY, 1, 16, 16, 16, layers=3)
+    cond = synth.model_params(w.shape, 3, (0, "tiny_sc"))
+    unc = synth.model_params(w.shape, 3, (0, "tiny_su"))
+    text, z, _, _ = synth.step_inputs(w)
+    cm, um = sfm.ModelWeights(to_device(cond)), sfm.ModelWeights(to_device(unc))
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw))
+    t = sfm.sfm_time_grid(4, 0.5, 1.75, 256 * 256)
+    g = [7.0, 7.0, 7.0, 3.0]
+    zd = z.to(DEV)
+    zo = torch.empty_like(zd)
+    sfm.sfm_sample(ctx_tiny, cm, um, text.to(DEV), zd, zo, t, g, 1, w.T, w.gh, w.gw, ws)
+    zh = zd.clone()
+    for i in range(4):
+        sfm.sfm_cfg_step(ctx_tiny, cm, um, text.to(DEV), zh, zh, float(t[i]), float(t[i] - t[i + 1]), g[i], 1, w.T,
+                         w.gh, w.gw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(zo, zh)
+    assert torch.equal(zd, z.to(DEV))          # the input latent is left alone
+    ref = OS.sample(np64(text), np64(z), list(t), g, oracle_model(cond), oracle_model(unc), w.gh, w.gw, O.TINY)
+    assert rel_l2(zo.cpu().numpy() - np64(z), ref - np64(z)) < 3e-2
+
+
 def test_cfg_step_full_properties(sfm, ctx_full):
     """The 34-layer, two-weight-set step at 1024^2 (the timed workload):
     finite, deterministic, and z' = z + dt (v_u + 4 (v_c - v_u)) holds for the
