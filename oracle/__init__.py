@@ -43,6 +43,8 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
   model_velocity         zero-layer reduction to the final layer of the embedding
   euler_cfg, cfg_step    closed forms; uncond ignores text; guidance 1 gives cond
   param_count            the ~9.3B of the spec table
+  text_projection        feature width of the cache page; exact scale invariance
+                         (eps 0); the textbook product when quantisation is exact
   sampler.time_grid      endpoints, order, closed-form median sigmoid(log 2) = 2/3,
                          symmetry without shift, scipy's normal quantile
   sampler presets        the research note's preset table (tests/golden)

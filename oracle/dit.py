@@ -121,6 +121,28 @@ def fp8_linear(a_bf16, w_codes, w_scale):
     return acc * sa[:, None] * np.asarray(w_scale, np.float64)[None, :]
 
 
+# --------------------------------------------------------------------------- text conditioning
+
+TEXT_FEATURES = 13 * 4096   # [Tuner] "Text embed cache": 13 Qwen hidden states of width 4096
+
+
+def text_projection(raw, norm_w_bf16, proj_codes, proj_scale, eps=1e-6):
+    """Projected text conditioning from the raw text-encoder features.
+
+    [Tuner] "Text embed cache": the text encoder output concatenates 13 Qwen
+    hidden states (13 * 4096 = 53,248 fp32 values per token); the
+    transformer's frozen llm_cond_norm and llm_cond_proj layers project them to
+    the bf16 conditioning the blocks consume (4608 wide).  Reading:
+    llm_cond_norm is an RMSNorm over the feature axis with a learnable weight
+    (eps 1e-6), stored in bf16; llm_cond_proj is a linear map without bias with
+    FP8-E4M3 weights and per-output-channel scales, fed like every FP8
+    projection (per-token E4M3 quantisation of its input); the output is
+    rounded to bf16.  raw float [M, K], norm_w [K]; returns bf16 values [M, N].
+    """
+    h = bf16_round(rms_normalize(raw, eps) * np.asarray(norm_w_bf16, np.float64))
+    return bf16_round(fp8_linear(h, proj_codes, proj_scale))
+
+
 def nf4_linear(a_bf16, packed, absmax, n, k):
     """y = a @ bf16(W_nf4)^T: NF4 weights dequantised to bf16 operands, bf16 input."""
     w = bf16_round(nf4_dequant_f32(packed, absmax, n, k).astype(np.float64))

@@ -436,3 +436,44 @@ def test_fp8_block_update_is_ill_conditioned():
         change[fmt] = np.linalg.norm((out - xp) - (ref - xx)) / np.linalg.norm(ref - xx)
     assert change["fp8"] > 2e-2
     assert change["nf4"] < change["fp8"] / 2
+
+
+# --------------------------------------------------------------------------- text projection
+
+def test_text_features_width_matches_the_cache_page():
+    import json
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "text_cache.json")))
+    assert O.TEXT_FEATURES == 53248
+    # the page's raw cache: 53,248 fp32 per token, about 0.203 MiB
+    assert abs(O.TEXT_FEATURES * 4 / 2 ** 20 - 0.203) < 5e-4
+    assert gold  # the fixture's own checks live in the cache-size test
+
+
+def test_text_projection_is_scale_invariant_without_eps():
+    rng = np.random.default_rng(41)
+    raw = rng.normal(0, 1, (3, 512)).astype(np.float32)
+    g = N.bf16_round(1 + rng.normal(0, 0.05, 512))
+    wq = N.e4m3_encode(rng.normal(0, 200, (16, 512)))
+    ws = rng.uniform(1e-4, 1e-3, 16).astype(np.float32)
+    a = O.text_projection(raw, g, wq, ws, eps=0.0)
+    b = O.text_projection(raw * np.float32(1024.0), g, wq, ws, eps=0.0)
+    assert np.array_equal(a, b)
+
+
+def test_text_projection_exact_case_is_a_plain_matmul():
+    """Constant raw rows normalise to +-1; with power-of-two norm weights the
+    per-token E4M3 quantisation is exact, so the projection is the textbook
+    product with the dequantised weight (then one bf16 rounding)."""
+    rng = np.random.default_rng(42)
+    K, Nn = 256, 24
+    raw = np.zeros((3, K), np.float32)
+    raw[0] = 2.0 ** 20
+    raw[1] = -(2.0 ** 22)
+    raw[2] = 3.0 * 2.0 ** 21
+    g = 2.0 ** rng.integers(-6, 2, K).astype(np.float64)
+    wq = N.e4m3_encode(rng.normal(0, 100, (Nn, K)))
+    ws = (2.0 ** rng.integers(-12, -6, Nn)).astype(np.float32)
+    y = O.text_projection(raw, g, wq, ws)
+    h = np.sign(raw[:, :1]).astype(np.float64) * g[None, :]
+    ref = N.bf16_round(np.matmul(h, N.fp8_dequant_f32(wq, ws).astype(np.float64).T))
+    assert np.array_equal(y, ref)
