@@ -136,6 +136,22 @@ def block_bench(sfm, synth, ctx, name, iters=5):
             "weights": w.wfmt}
 
 
+def text_project_bench(sfm, synth, ctx, M=512, iters=10):
+    """The text-conditioning projection of one 512-token prompt: 53,248 raw
+    features per token to 4608 (RMSNorm + E4M3 + FP8 GEMM, K 53,248)."""
+    import torch
+    k, D = synth.TEXT_FEATURES, 4608
+    norm_w, wq, ws = synth.text_proj_params(D, k, ("bench_tp",), device="cuda")
+    raw = synth.text_raw(M, k, ("bench_tp",), device="cuda")
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, wq, ws)
+    out = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
+    wsp = sfm.workspace(sfm.lib().sfm_text_project_workspace_bytes(M, k))
+    sec = time_gpu(lambda: sfm.sfm_text_project(ctx, raw, norm_w, w, out, wsp), iters)
+    fl = 2.0 * M * k * D
+    return {"workload": f"{M} tokens x {k} raw features -> {D}", "us": round(sec * 1e6, 1),
+            "tflops": round(fl / sec / 1e12, 2), "frac_fp8_peak": round(fl / sec / 1e12 / FP8_PEAK_TFLOPS, 4)}
+
+
 ROOF_SHAPE = (4608, 4608, 12288)   # M, K, F of the dominant launch (gate/up + SwiGLU, conditional pass)
 ROOF_SOURCES = ("stream_flow_matching_amd/csrc/k_gemm_fp8.hip", "stream_flow_matching_amd/csrc/gemm_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_swiglu_4608x24576x4608_traffic.md")
@@ -380,6 +396,7 @@ def main():
     if not args.no_extra:
         for name in ("block_1024", "block_2048", "block_6to1_nf4"):
             extra[name] = block_bench(sfm, synth, ctx, name)
+        extra["text_projection_512"] = text_project_bench(sfm, synth, ctx)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample)
 
     line = {

@@ -279,7 +279,27 @@ int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, co
                        int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
                        void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded);
 
-/* ---------------------------------------------------------------- sampler */
+/* ---------------------------------------------------------------- text conditioning */
+
+/* Workspace bytes of sfm_text_project for M tokens of k_raw features. */
+size_t sfm_text_project_workspace_bytes(int M, int k_raw);
+
+/* Projected text conditioning from raw text-encoder features (SimpleTuner
+ * Ideogram 4 quick start, "Text embed cache": the text encoder concatenates 13
+ * Qwen hidden states, 13 * 4096 = 53,248 fp32 values per token, and the
+ * transformer's frozen llm_cond_norm and llm_cond_proj project them to the
+ * conditioning the blocks consume).  text_out[m] = bf16(FP8 linear(bf16(
+ * raw[m] / sqrt(mean(raw[m]^2) + eps) * norm_w))): RMSNorm with a weight,
+ * then a projection without bias, its input quantised per token to E4M3 like
+ * every FP8 projection.  raw fp32 [M][k] (row-major), norm_w bf16 [k],
+ * proj FP8 [emb_dim][k] with per-channel scales, text_out bf16 [M][emb_dim].
+ * k = proj->k must be a multiple of 256 in [256, 65536].  M rows are
+ * independent (batch and tokens flattened).  Errors: SFM_E_INVALID_ARG (NULL
+ * or non-FP8 weight), SFM_E_SHAPE, SFM_E_WORKSPACE, SFM_E_ALIGN, SFM_E_DEVICE. */
+int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
+                     uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- sampler *//* ---------------------------------------------------------------- sampler */
 
 /* Time grid of the logit-normal schedule (research note, "Training method":
  * logit-normal noise schedule with parameters (mu, std), mu shifted by

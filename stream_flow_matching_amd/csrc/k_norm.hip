@@ -113,6 +113,55 @@ __global__ __launch_bounds__(kRowThreads) void adaln_kernel(const uint16_t* __re
     }
 }
 
+// RMSNorm with a weight over a long fp32 row, rounded to bf16, then per-row
+// E4M3 quantisation: the input side of the text-conditioning projection
+// (SimpleTuner Ideogram 4 quick start, "Text embed cache": 13 x 4096 fp32
+// features per token go through the frozen llm_cond_norm before
+// llm_cond_proj).  One workgroup per row, three passes: the sum of squares from
+// global memory, h = bf16(x * rinv * w) into LDS (cols * 2 bytes) with its
+// absolute maximum, then the codes from LDS.  Thread t owns the 4-element
+// groups 4 (t + 256 j) in every pass, so the LDS row needs no barrier between
+// writing and reading back.  cols % 4 == 0.
+__global__ __launch_bounds__(kRowThreads) void rmsnorm_f32_quant_kernel(const float* __restrict__ x, int cols,
+                                                                        const uint16_t* __restrict__ w,
+                                                                        uint8_t* __restrict__ q,
+                                                                        float* __restrict__ s, float eps) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t hrow[];
+    __shared__ float red[kRowWaves];
+    const int64_t m = blockIdx.x;
+    const float* row = x + m * cols;
+    float ss = 0.f;
+    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
+        const float4 v = *reinterpret_cast<const float4*>(row + i);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = block_sum<kRowWaves>(ss, red);
+    const float rinv = 1.0f / sqrtf(ss / (float)cols + eps);
+    float amax = 0.f;
+    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
+        const float4 v = *reinterpret_cast<const float4*>(row + i);
+        const uint2 g = *reinterpret_cast<const uint2*>(w + i);
+        const float h0 = round_bf16((v.x * rinv) * __uint_as_float(g.x << 16));
+        const float h1 = round_bf16((v.y * rinv) * __uint_as_float(g.x & 0xFFFF0000u));
+        const float h2 = round_bf16((v.z * rinv) * __uint_as_float(g.y << 16));
+        const float h3 = round_bf16((v.w * rinv) * __uint_as_float(g.y & 0xFFFF0000u));
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(h0), fabsf(h1)), fmaxf(fabsf(h2), fabsf(h3))));
+        *reinterpret_cast<uint2*>(hrow + i) = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+    }
+    amax = block_max<kRowWaves>(amax, red);
+    const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
+        const uint2 h = *reinterpret_cast<const uint2*>(hrow + i);
+        uint32_t c = 0;
+        c = cvt_fp8x2<false>(clamp448(__uint_as_float(h.x << 16) * inv),
+                             clamp448(__uint_as_float(h.x & 0xFFFF0000u) * inv), c);
+        c = cvt_fp8x2<true>(clamp448(__uint_as_float(h.y << 16) * inv),
+                            clamp448(__uint_as_float(h.y & 0xFFFF0000u) * inv), c);
+        *reinterpret_cast<uint32_t*>(q + m * cols + i) = c;
+    }
+    if (threadIdx.x == 0) s[m] = amax / 448.0f;
+}
+
 template <int MAXC>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t* __restrict__ a, int cols,
                                                                  uint8_t* __restrict__ q, float* __restrict__ s) {
@@ -255,6 +304,21 @@ hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, uint8_t* q, 
         hipLaunchKernelGGL(quant_rows_kernel<8>, dim3(rows), dim3(kRowThreads), 0, st, a, cols, q, s);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_f32_quant(const float* x, int rows, int cols, const uint16_t* w, uint8_t* q, float* s,
+                                    float eps, hipStream_t st) {
+    if (rows == 0) return hipSuccess;
+    if (cols % 4 || cols > 65536) return hipErrorInvalidValue;
+    const size_t shm = (size_t)cols * 2;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)rmsnorm_f32_quant_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  65536 * 2);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(rmsnorm_f32_quant_kernel, dim3(rows), dim3(kRowThreads), shm, st, x, cols, w, q, s, eps);
     return hipGetLastError();
 }
 

@@ -522,6 +522,40 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
     return SFM_OK;
 }
 
+size_t sfm_text_project_workspace_bytes(int M, int k_raw) {
+    if (M < 0 || k_raw < 0) return 0;
+    Carve c(nullptr);
+    c.take<uint8_t>((size_t)M * k_raw);
+    c.take<float>((size_t)M);
+    return c.off + 256;
+}
+
+int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
+                     uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    if (!proj) return fail(SFM_E_INVALID_ARG, "proj is NULL");
+    const int D = ctx->dims.emb_dim, K = proj->k;
+    if (K < 256 || K % 256 || K > 65536)
+        return fail(SFM_E_SHAPE, "feature width %d: need a multiple of 256 in [256, 65536]", K);
+    SFM_CHECK(check_qweight(proj, SFM_W_FP8_E4M3, D, K, "proj"));
+    SFM_CHECK(check_ptr(raw, "raw"));
+    SFM_CHECK(check_ptr(norm_w, "norm_w"));
+    SFM_CHECK(check_ptr(text_out, "text_out"));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    if (M < 0) return fail(SFM_E_SHAPE, "M < 0");
+    const size_t need = sfm_text_project_workspace_bytes(M, K);
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    if (M == 0) return SFM_OK;
+    Carve c(ws);
+    uint8_t* codes = c.take<uint8_t>((size_t)M * K);
+    float* scales = c.take<float>((size_t)M);
+    const hipStream_t st = (hipStream_t)stream;
+    SFM_LAUNCH(launch_rmsnorm_f32_quant(raw, M, K, norm_w, codes, scales, ctx->dims.eps, st));
+    SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, proj->scale, text_out, nullptr,
+                               nullptr, 0, M, D, K, M, st));
+    return SFM_OK;
+}
+
 int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                      uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh, int gw, void* stream) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");

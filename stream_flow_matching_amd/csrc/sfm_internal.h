@@ -141,6 +141,9 @@ hipError_t launch_adaln_bf16(const uint16_t* x, int64_t rows_per_batch_in, int64
                              const float* scale, int64_t scale_stride, uint16_t* h, int B, int D, float eps,
                              hipStream_t st);
 hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, uint8_t* q, float* s, hipStream_t st);
+// h = bf16(x / sqrt(mean(x^2) + eps) * w) per fp32 row, then E4M3 codes + alpha/448; cols % 4 == 0, <= 65536
+hipError_t launch_rmsnorm_f32_quant(const float* x, int rows, int cols, const uint16_t* w, uint8_t* q, float* s,
+                                    float eps, hipStream_t st);
 hipError_t launch_timestep_embed(float t, float* e, int B, int dim, hipStream_t st);
 
 // k_gemm_fp8.hip

@@ -101,6 +101,8 @@ SIGNATURES = {
     "sfm_cfg_step_timed": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
                                 _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P),
                                 ctypes.POINTER(_P), _I, ctypes.POINTER(_I)]),
+    "sfm_text_project_workspace_bytes": (_SZ, [_I, _I]),
+    "sfm_text_project": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _I, _P, _SZ, _P]),
     "sfm_time_grid": (_I, [_I, ctypes.c_double, ctypes.c_double, _I64, _P]),
     "sfm_preset": (_I, [_I, ctypes.POINTER(sfm_preset_info)]),
     "sfm_preset_schedule": (_I, [_I, _I, _I, _P, _P, _I]),
@@ -298,6 +300,15 @@ def sfm_cfg_step_timed(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z
                                     float(guidance), B, T, gh, gw, _ptr(v_c_out), _ptr(v_u_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream), b, e, n, ctypes.byref(rec)))
     return rec.value
+
+
+def sfm_text_project(ctx, raw, norm_w, proj, text_out, ws=None, stream=None):
+    """raw fp32 [..., k] -> text_out bf16 [..., emb_dim]; proj a qweight (FP8)."""
+    M = raw.numel() // raw.shape[-1]
+    if ws is None:
+        ws = workspace(lib().sfm_text_project_workspace_bytes(M, raw.shape[-1]), raw.device)
+    _check(lib().sfm_text_project(ctx.handle, _ptr(raw), _ptr(norm_w), ctypes.byref(proj), _ptr(text_out), M,
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def sfm_time_grid(n_steps, mu, std_dev, num_pixels):

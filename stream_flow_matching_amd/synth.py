@@ -158,6 +158,22 @@ class BlockParams:
     mod_b: torch.Tensor       # f32 [4D]
 
 
+TEXT_FEATURES = 13 * 4096   # raw text-encoder width: 13 hidden states of 4096
+
+
+def text_proj_params(D, k, key, device="cpu"):
+    """Text-conditioning projection: norm weight 1 + N(0, 0.02) (bf16) and FP8
+    projection weights [D][k] from N(0, 0.02) with per-channel scales."""
+    norm_w = bf16_normal((k,), key + ("norm",), 0.02, 1.0, device)
+    wq, ws = fp8_weight(D, k, key + ("proj",), device=device)
+    return norm_w, wq, ws
+
+
+def text_raw(M, k, key, device="cpu"):
+    """Raw text-encoder features, fp32 N(0, 1) [M][k]."""
+    return randn((M, k), key + ("raw",), 1.0, device)
+
+
 def block_params(shape: Shape, key, fmt="fp8", device="cpu") -> BlockParams:
     D, F = shape.emb_dim, shape.intermediate
     mk = fp8_weight if fmt == "fp8" else nf4_weight

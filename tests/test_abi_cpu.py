@@ -184,3 +184,11 @@ def test_sampler_argument_checks(S):
                         None) == -1
     assert L.sfm_sample(None, None, None, None, good, good, tt.ctypes.data_as(P), gg.ctypes.data_as(P), 0, 1, 0,
                         16, 16, good, 0, None) == -1
+
+
+def test_text_project_argument_checks(S):
+    L = S.lib()
+    P = ctypes.c_void_p
+    good = P(1 << 20)
+    assert L.sfm_text_project_workspace_bytes(512, 53248) >= 512 * 53248 + 512 * 4
+    assert L.sfm_text_project(None, good, good, None, good, 4, good, 1 << 30, None) == -1

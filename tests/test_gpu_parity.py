@@ -266,6 +266,41 @@ def test_linear_fp8_gated_residual_three_batches_per_tile(sfm, ctx_full, M, Nw, 
     assert rel_l2(got - np64(resid[rows]), ref - np64(resid[rows])) < 1e-2
 
 
+# --------------------------------------------------------------------------- text conditioning projection
+
+@pytest.mark.parametrize("M,k", [(37, 1024), (1, 256), (300, 2048)])
+def test_text_project_tiny_width(sfm, ctx_tiny, M, k):
+    """RMSNorm with weight + per-token E4M3 + FP8 projection to the tiny model
+    width, all rows (ragged M) against the oracle."""
+    _say("text project", M, k)
+    norm_w, wq, ws = synth.text_proj_params(512, k, ("tp", k))
+    raw = synth.text_raw(M, k, ("tp", M, k))
+    keep = (wq.to(DEV), ws.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    out = torch.empty(M, 512, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_text_project(ctx_tiny, raw.to(DEV), norm_w.to(DEV), w, out)
+    torch.cuda.synchronize()
+    ref = O.text_projection(raw.numpy(), np64(norm_w), npu8(wq), ws.numpy())
+    assert rel_l2(np64(out), ref) < 2e-3
+
+
+def test_text_project_full_width_sampled(sfm, ctx_full):
+    """The page's shape: 512 tokens of 13 x 4096 = 53,248 raw features to 4608;
+    sampled rows against the oracle."""
+    _say("text project full")
+    M, k = 512, synth.TEXT_FEATURES
+    norm_w, wq, ws = synth.text_proj_params(4608, k, ("tpf",))
+    raw = synth.text_raw(M, k, ("tpf",))
+    keep = (wq.to(DEV), ws.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    out = torch.empty(M, 4608, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_text_project(ctx_full, raw.to(DEV), norm_w.to(DEV), w, out)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 256, 511])
+    ref = O.text_projection(raw[rows].numpy(), np64(norm_w), npu8(wq), ws.numpy())
+    assert rel_l2(np64(out[rows]), ref) < 2e-3
+
+
 # --------------------------------------------------------------------------- a12 NF4 linear
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
