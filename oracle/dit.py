@@ -349,6 +349,20 @@ def block_forward(x_bf16, c, wts: BlockWeights, T, gh, gw, dims: Dims, rows=None
 
 # --------------------------------------------------------------------------- model
 
+def block_forward_varlen(x_bf16, c, wts: BlockWeights, T, text_lens, gh, gw, dims: Dims):
+    """A batch whose text prefixes are padded to T rows: sample b holds
+    text_lens[b] text rows, then padding up to row T, then its image rows.
+    Each sample is computed alone on its own tokens (its first text_lens[b]
+    rows and its image rows, with T = text_lens[b]); padding rows come back as
+    NaN (their value is unspecified).  Returns float64 [B, T + gh*gw, D]."""
+    x = np.asarray(x_bf16, np.float64)
+    out = np.full_like(x, np.nan)
+    for b, tb in enumerate(text_lens):
+        rows = np.r_[0:tb, T:x.shape[1]]
+        out[b, rows] = block_forward(x[b:b + 1, rows], c[b:b + 1], wts, int(tb), gh, gw, dims)[0]
+    return out
+
+
 def timestep_embedding(t, dim=512):
     """Sinusoidal embedding of the flow-matching time t in [0, 1] (DiT lineage,
     [Note] background).  e = [cos(1000 t f_i), sin(1000 t f_i)], f_i =
@@ -427,6 +441,20 @@ def cfg_step(text_bf16, z, t, dt, guidance, cond: ModelWeights, uncond: ModelWei
     ([Note] "Training method": asymmetric CFG; [Tuner] "Validation": a separate
     image-only unconditional transformer).  Returns (z', v, v_c, v_u)."""
     v_c = model_velocity(text_bf16, z, t, cond, gh, gw, dims)
+    v_u = model_velocity(None, z, t, uncond, gh, gw, dims)
+    z2, v = euler_cfg(z, v_c, v_u, guidance, dt)
+    return z2, v, v_c, v_u
+
+
+def cfg_step_varlen(text_bf16, text_lens, z, t, dt, guidance, cond: ModelWeights, uncond: ModelWeights, gh, gw,
+                    dims: Dims):
+    """Guided step for prompts of different lengths (text padded to T rows):
+    each sample's conditional velocity uses only its own text_lens[b] text
+    rows; the unconditional pass has no text.  Returns (z', v, v_c, v_u)."""
+    z = np.asarray(z, np.float64)
+    text = np.asarray(text_bf16, np.float64)
+    v_c = np.concatenate([model_velocity(text[b:b + 1, :int(tb)] if tb > 0 else None, z[b:b + 1], [t[b]], cond, gh,
+                                         gw, dims) for b, tb in enumerate(text_lens)])
     v_u = model_velocity(None, z, t, uncond, gh, gw, dims)
     z2, v = euler_cfg(z, v_c, v_u, guidance, dt)
     return z2, v, v_c, v_u

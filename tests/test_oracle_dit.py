@@ -477,3 +477,47 @@ def test_text_projection_exact_case_is_a_plain_matmul():
     h = np.sign(raw[:, :1]).astype(np.float64) * g[None, :]
     ref = N.bf16_round(np.matmul(h, N.fp8_dequant_f32(wq, ws).astype(np.float64).T))
     assert np.array_equal(y, ref)
+
+
+# --------------------------------------------------------------------------- variable text lengths
+
+def test_block_varlen_with_full_lengths_is_the_batched_block():
+    rng = np.random.default_rng(51)
+    wts = _tiny_block(rng)
+    x = N.bf16_round(rng.normal(0, 1, (2, 3 + 4, 512)))
+    c = rng.normal(0, 1, (2, 512))
+    a = O.block_forward_varlen(x, c, wts, 3, [3, 3], 2, 2, O.TINY)
+    b = O.block_forward(x, c, wts, 3, 2, 2, O.TINY)
+    assert np.array_equal(a, b)
+
+
+def test_block_varlen_padding_rows_do_not_reach_the_sample():
+    """Valid rows of a sample depend only on its own text and image rows: the
+    padding content changes nothing, and a sample with a shorter text equals
+    the same sample stored unpadded."""
+    rng = np.random.default_rng(52)
+    wts = _tiny_block(rng)
+    T, lens = 5, [2, 5, 0]
+    x = N.bf16_round(rng.normal(0, 1, (3, T + 4, 512)))
+    c = rng.normal(0, 1, (3, 512))
+    a = O.block_forward_varlen(x, c, wts, T, lens, 2, 2, O.TINY)
+    x2 = x.copy()
+    x2[0, 2:T] = N.bf16_round(rng.normal(0, 3, (T - 2, 512)))
+    x2[2, 0:T] = N.bf16_round(rng.normal(0, 3, (T, 512)))
+    b = O.block_forward_varlen(x2, c, wts, T, lens, 2, 2, O.TINY)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    alone = O.block_forward(np.concatenate([x[0:1, :2], x[0:1, T:]], axis=1), c[0:1], wts, 2, 2, 2, O.TINY)
+    assert np.array_equal(np.concatenate([a[0:1, :2], a[0:1, T:]], axis=1), alone)
+    assert np.isnan(a[0, 2:T]).all() and np.isnan(a[2, :T]).all()
+
+
+def test_cfg_step_varlen_with_full_lengths_is_the_batched_step():
+    rng = np.random.default_rng(53)
+    cond, unc = _tiny_model(rng, 1), _tiny_model(rng, 1)
+    z = rng.normal(0, 1, (2, 4, 128))
+    text = N.bf16_round(rng.normal(0, 1, (2, 3, 512)))
+    a = O.cfg_step_varlen(text, [3, 3], z, [0.6, 0.6], 0.125, 4.0, cond, unc, 2, 2, O.TINY)
+    b = O.cfg_step(text, z, [0.6, 0.6], 0.125, 4.0, cond, unc, 2, 2, O.TINY)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
