@@ -279,7 +279,39 @@ int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, co
                        int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
                        void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded);
 
-/* ---------------------------------------------------------------- text conditioning */
+/* ---------------------------------------------------------------- variable text lengths */
+
+/* Batches of prompts with different text lengths.  The text prefixes are
+ * padded to T rows in memory ([B][T + gh*gw][D] as everywhere); text_lens is
+ * a host array of B values in [0, T] (B <= 64): sample b's text is rows
+ * [0, text_lens[b]) of its prefix, rows [text_lens[b], T) are padding.  Each
+ * sample's text and image rows come out as if the sample ran alone with its
+ * own text_lens[b] text tokens: its image positions start at text_lens[b]
+ * (research note, "Model architecture": image tokens at (t, h, w) after the
+ * 1-D text positions) and attention masks the padding keys (key tiles wholly
+ * inside the padding are skipped).  Padding rows' own outputs are unspecified
+ * (finite for finite inputs).  Errors as the uniform calls, plus SFM_E_SHAPE
+ * for a length outside [0, T] or B > 64 and SFM_E_INVALID_ARG for NULL
+ * text_lens.  Workspaces are those of the uniform calls. */
+int sfm_qk_norm_rope_varlen(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm,
+                            const uint16_t* k_norm, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T,
+                            const int32_t* text_lens, int gh, int gw, void* stream);
+/* L = T + image tokens per sample; requires T < L. */
+int sfm_attention_varlen(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o,
+                         int B, int L, int T, const int32_t* text_lens, void* stream);
+int sfm_block_forward_varlen(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in,
+                             uint16_t* x_out, const float* c, int B, int T, const int32_t* text_lens, int gh, int gw,
+                             void* ws, size_t ws_bytes, void* stream);
+int sfm_model_velocity_varlen(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                              const int32_t* text_lens, const float* latent, float t, float* v_out, int B, int T,
+                              int gh, int gw, void* ws, size_t ws_bytes, void* stream);
+/* The lengths apply to the conditional pass; the unconditional pass has no text. */
+int sfm_cfg_step_varlen(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                        const uint16_t* text, const int32_t* text_lens, const float* z, float* z_out, float t, float dt,
+                        float guidance, int B, int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- text conditioning *//* ---------------------------------------------------------------- text conditioning */
 
 /* Workspace bytes of sfm_text_project for M tokens of k_raw features. */
 size_t sfm_text_project_workspace_bytes(int M, int k_raw);
@@ -343,6 +375,11 @@ int sfm_preset_schedule(int preset, int height_px, int width_px, double* t_out, 
 int sfm_sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
                const uint16_t* text, const float* z, float* z_out, const double* t, const float* guidance,
                int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream);
+/* sfm_sample over sfm_cfg_step_varlen (per-sample text lengths, see above). */
+int sfm_sample_varlen(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                      const uint16_t* text, const int32_t* text_lens, const float* z, float* z_out, const double* t,
+                      const float* guidance, int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* ---------------------------------------------------------------- errors */
 const char* sfm_status_string(int status);

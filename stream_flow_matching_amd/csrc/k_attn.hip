@@ -87,7 +87,7 @@ __device__ __forceinline__ float col_max(float x) {
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
-    uint16_t* __restrict__ o, int L, int Lp, int H, int nqb) {
+    uint16_t* __restrict__ o, int L, int Lp, int H, int nqb, int T, TextLens lens, int varlen) {
     __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kKTile];
     __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kKTile];
 
@@ -98,6 +98,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qb = bid % nqb;
     const int bh = bid / nqb;  // b * H + h
     const int h = bh % H, b = bh / H;
+    const int Tb = varlen ? lens.len[b] : T;  // this sample's text rows; keys [Tb, T) are padding
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -189,12 +190,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (key0 + kKB > L) {  // ragged last tile: mask keys >= L
+        // mask keys >= L (ragged last tile) and the sample's text padding [Tb, T)
+        if (key0 + kKB > L || (Tb < T && key0 < T && key0 + kKB > Tb)) {
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (key0 + t4 * 16 + 4 * lg + r >= L)
+                    if (const int key = key0 + t4 * 16 + 4 * lg + r; key >= L || (key >= Tb && key < T))
 #pragma unroll
                         for (int qt = 0; qt < NQT; ++qt) s[qt][t4][r] = -INFINITY;
         }
@@ -271,18 +273,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // Two LDS stages: tile t lives in stage t & 1; the loads of tile t + 1 run
     // during the compute of tile t; one barrier per tile.
-    const int nkt = (L + kKB - 1) / kKB;
-    ld.issue(st0, 0);
+    // Key tiles wholly inside the padding [Tb, T) are skipped: tile e of the walk is key tile e
+    // before the padding and e + nskip after it.
+    const int skip0 = (Tb + kKB - 1) / kKB, nskip = max(0, T / kKB - skip0);
+    const int nkt = (L + kKB - 1) / kKB - nskip;
+    auto key_of = [&](int e) { return (e < skip0 ? e : e + nskip) * kKB; };
+    ld.issue(st0, key_of(0));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nkt; kt += 2) {
-        if (kt + 1 < nkt) ld.issue(st1, (kt + 1) * kKB);
-        compute(st0, kt * kKB);
+        if (kt + 1 < nkt) ld.issue(st1, key_of(kt + 1));
+        compute(st0, key_of(kt));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kt + 1 >= nkt) break;
-        if (kt + 2 < nkt) ld.issue(st0, (kt + 2) * kKB);
-        compute(st1, (kt + 1) * kKB);
+        if (kt + 2 < nkt) ld.issue(st0, key_of(kt + 2));
+        compute(st1, key_of(kt + 1));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -311,11 +317,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o, int B, int L,
-                            int H, hipStream_t st) {
+                            int H, int T, const TextLens* lens, hipStream_t st) {
     if (L == 0) return hipSuccess;
     const int Lp = padded_len(L);
     const int nqb = Lp / kQB;
-    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(512), 0, st, q, k, vt, o, L, Lp, H, nqb);
+    TextLens tl{};
+    if (lens) tl = *lens;
+    hipLaunchKernelGGL(attn_kernel, dim3(nqb * H * B), dim3(512), 0, st, q, k, vt, o, L, Lp, H, nqb, T, tl,
+                       lens ? 1 : 0);
     return hipGetLastError();
 }
 

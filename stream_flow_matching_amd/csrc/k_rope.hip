@@ -35,12 +35,15 @@ __device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-__device__ __forceinline__ int axis_pos(int l, int T, int gw, int axis) {
+// position on one axis of row l of a sample whose text prefix has T rows, the
+// first Tb of them real text: text (and padding) rows l -> l, image token i =
+// l - T at (Tb, Tb + i / gw, Tb + i % gw)
+__device__ __forceinline__ int axis_pos(int l, int T, int Tb, int gw, int axis) {
     if (l < T) return l;
     const int i = l - T;
-    if (axis == 0) return T;
-    if (axis == 1) return T + i / gw;
-    return T + i % gw;
+    if (axis == 0) return Tb;
+    if (axis == 1) return Tb + i / gw;
+    return Tb + i % gw;
 }
 
 // x of lane (l & ~15) | ((l + 8) & 15): the chunk eight 16-byte chunks away in a 16-lane row
@@ -77,11 +80,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
                                                            const float* __restrict__ cos_t,
                                                            const float* __restrict__ sin_t, uint16_t* __restrict__ q,
                                                            uint16_t* __restrict__ k, uint16_t* __restrict__ vt, int T,
-                                                           int gw, int L, int Lp, int H, float eps) {
+                                                           int gw, int L, int Lp, int H, float eps, TextLens lens,
+                                                           int varlen) {
     __shared__ uint16_t vs[256][kTok + 2];  // [d][token] fp16 bits, padded row
     const int l0 = blockIdx.x * kTok;
     const int h = blockIdx.y;
     const int b = blockIdx.z;
+    const int Tb = varlen ? lens.len[b] : T;
     const int D = H * 256;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row_stride = 3 * (int64_t)D;
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[v][e] = u[v][e] * rn * (part == 0 ? gq[e] : gk[e]);
             const int lc = min(l, L - 1);
-            const int pa = axis_pos(lc, T, gw, axA), pb = axis_pos(lc, T, gw, axB);
+            const int pa = axis_pos(lc, T, Tb, gw, axA), pb = axis_pos(lc, T, Tb, gw, axB);
             const float4 ca = *reinterpret_cast<const float4*>(cos_t + pa * 64 + j0);
             const float4 cb = *reinterpret_cast<const float4*>(cos_t + pb * 64 + j0 + 4);
             const float4 sa = *reinterpret_cast<const float4*>(sin_t + pa * 64 + j0);
@@ -177,11 +182,13 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
 
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const uint16_t* kn, const float* cos_t,
                                const float* sin_t, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh,
-                               int gw, int H, float eps, hipStream_t st) {
+                               int gw, int H, float eps, const TextLens* lens, hipStream_t st) {
     const int L = T + gh * gw;
     const int Lp = padded_len(L);
+    TextLens tl{};
+    if (lens) tl = *lens;
     hipLaunchKernelGGL(qk_norm_rope_kernel, dim3(Lp / kTok, H, B), dim3(256), 0, st, qkv, qn, kn, cos_t, sin_t, q,
-                       k, vt, T, gw, L, Lp, H, eps);
+                       k, vt, T, gw, L, Lp, H, eps, tl, lens ? 1 : 0);
     return hipGetLastError();
 }
 

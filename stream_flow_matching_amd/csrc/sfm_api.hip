@@ -220,7 +220,8 @@ struct LaunchTimer {
 
 // Enqueue one block; arguments already checked.
 int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
-              const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, LaunchTimer* timer = nullptr) {
+              const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
+              LaunchTimer* timer = nullptr) {
     const bool timed = timer && timer->used < timer->n;
     auto mark = [&](void* const* ev) -> hipError_t {
         return timed ? hipEventRecord((hipEvent_t)ev[timer->used], st) : hipSuccess;
@@ -238,8 +239,8 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
         SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
     }
     SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T, gh,
-                                   gw, H, d->eps, st));
-    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, st));
+                                   gw, H, d->eps, lens, st));
+    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
     if (fmt == SFM_W_FP8_E4M3) {
         SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
@@ -305,8 +306,22 @@ int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
     return SFM_OK;
 }
 
+// Per-sample text lengths from the caller's host array: B <= kMaxVarlenBatch, 0 <= len <= T.
+int make_lens(const int32_t* text_lens, int B, int T, TextLens* out) {
+    if (!text_lens) return fail(SFM_E_INVALID_ARG, "text_lens is NULL");
+    if (B > kMaxVarlenBatch) return fail(SFM_E_SHAPE, "per-sample text lengths need B <= %d", kMaxVarlenBatch);
+    *out = TextLens{};
+    for (int b = 0; b < B; ++b) {
+        if (text_lens[b] < 0 || text_lens[b] > T)
+            return fail(SFM_E_SHAPE, "text_lens[%d] = %d outside [0, T = %d]", b, text_lens[b], T);
+        out->len[b] = text_lens[b];
+    }
+    return SFM_OK;
+}
+
 int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent, float t,
-              float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st, LaunchTimer* timer = nullptr) {
+              float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
+              LaunchTimer* timer = nullptr) {
     const sfm_dims* d = &ctx->dims;
     const int N = gh * gw, L = T + N, D = d->emb_dim, A = d->adaln_dim, C = d->latent_ch;
     StepWs w = plan_model(d, B, T, gh, gw, ws);
@@ -316,7 +331,7 @@ int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_
     if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
     SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
     for (int i = 0; i < mw->num_layers; ++i)
-        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, timer));
+        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, lens, timer));
     SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
     SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
     SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
@@ -564,7 +579,22 @@ int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t
     const char* ns[] = {"qkv", "q_norm", "k_norm", "q", "k", "vt"};
     for (int i = 0; i < 6; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
     SFM_LAUNCH(launch_qk_norm_rope(qkv, q_norm, k_norm, ctx->rope_cos, ctx->rope_sin, q, k, vt, B, T, gh, gw,
-                                   ctx->dims.num_heads, ctx->dims.eps, (hipStream_t)stream));
+                                   ctx->dims.num_heads, ctx->dims.eps, nullptr, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_qk_norm_rope_varlen(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm,
+                            const uint16_t* k_norm, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T,
+                            const int32_t* text_lens, int gh, int gw, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    TextLens lens;
+    SFM_CHECK(make_lens(text_lens, B, T, &lens));
+    const void* ps[] = {qkv, q_norm, k_norm, q, k, vt};
+    const char* ns[] = {"qkv", "q_norm", "k_norm", "q", "k", "vt"};
+    for (int i = 0; i < 6; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
+    SFM_LAUNCH(launch_qk_norm_rope(qkv, q_norm, k_norm, ctx->rope_cos, ctx->rope_sin, q, k, vt, B, T, gh, gw,
+                                   ctx->dims.num_heads, ctx->dims.eps, &lens, (hipStream_t)stream));
     return SFM_OK;
 }
 
@@ -576,7 +606,22 @@ int sfm_attention(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, 
     SFM_CHECK(check_ptr(vt, "vt"));
     SFM_CHECK(check_ptr(o, "o"));
     if (B < 1 || L < 1 || L > ctx->dims.max_text + 128 * 128) return fail(SFM_E_SHAPE, "B / L out of range");
-    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, (hipStream_t)stream));
+    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, 0, nullptr, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_attention_varlen(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o,
+                         int B, int L, int T, const int32_t* text_lens, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(check_ptr(q, "q"));
+    SFM_CHECK(check_ptr(k, "k"));
+    SFM_CHECK(check_ptr(vt, "vt"));
+    SFM_CHECK(check_ptr(o, "o"));
+    if (B < 1 || L < 1 || L > ctx->dims.max_text + 128 * 128) return fail(SFM_E_SHAPE, "B / L out of range");
+    if (T < 0 || T >= L) return fail(SFM_E_SHAPE, "text prefix T = %d must leave image keys (L = %d)", T, L);
+    TextLens lens;
+    SFM_CHECK(make_lens(text_lens, B, T, &lens));
+    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, T, &lens, (hipStream_t)stream));
     return SFM_OK;
 }
 
@@ -617,10 +662,14 @@ size_t sfm_block_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, i
     return plan_block(&ctx->dims, B, T, gh, gw, wfmt, nullptr).bytes;
 }
 
-int sfm_block_forward(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in, uint16_t* x_out,
-                      const float* c, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int block_forward(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in, uint16_t* x_out,
+                  const float* c, int B, int T, const int32_t* text_lens, int gh, int gw, void* ws, size_t ws_bytes,
+                  void* stream) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    TextLens lens;
+    if (text_lens) SFM_CHECK(make_lens(text_lens, B, T, &lens));
     int fmt = 0;
     SFM_CHECK(check_block_weights(&ctx->dims, w, &fmt));
     SFM_CHECK(check_ptr(x_in, "x_in"));
@@ -629,7 +678,20 @@ int sfm_block_forward(const sfm_context* ctx, const sfm_block_weights* w, const 
     SFM_CHECK(check_ptr(ws, "ws"));
     const size_t need = plan_block(&ctx->dims, B, T, gh, gw, fmt, nullptr).bytes;
     if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-    return run_block(ctx, w, fmt, x_in, x_out, c, B, T, gh, gw, ws, (hipStream_t)stream);
+    return run_block(ctx, w, fmt, x_in, x_out, c, B, T, gh, gw, ws, (hipStream_t)stream, text_lens ? &lens : nullptr);
+}
+}  // namespace
+
+int sfm_block_forward(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in, uint16_t* x_out,
+                      const float* c, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    return block_forward(ctx, w, x_in, x_out, c, B, T, nullptr, gh, gw, ws, ws_bytes, stream);
+}
+
+int sfm_block_forward_varlen(const sfm_context* ctx, const sfm_block_weights* w, const uint16_t* x_in,
+                             uint16_t* x_out, const float* c, int B, int T, const int32_t* text_lens, int gh, int gw,
+                             void* ws, size_t ws_bytes, void* stream) {
+    if (!text_lens) return fail(SFM_E_INVALID_ARG, "text_lens is NULL");
+    return block_forward(ctx, w, x_in, x_out, c, B, T, text_lens, gh, gw, ws, ws_bytes, stream);
 }
 
 size_t sfm_step_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw) {
@@ -643,10 +705,14 @@ size_t sfm_step_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, in
     return c.off + 256;
 }
 
-int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent,
-                       float t, float* v_out, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                   const int32_t* text_lens, const float* latent, float t, float* v_out, int B, int T, int gh, int gw,
+                   void* ws, size_t ws_bytes, void* stream) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    TextLens lens;
+    if (text_lens) SFM_CHECK(make_lens(text_lens, B, T, &lens));
     SFM_CHECK(check_model_weights(&ctx->dims, mw));
     if (T > 0) SFM_CHECK(check_ptr(text, "text"));
     SFM_CHECK(check_ptr(latent, "latent"));
@@ -655,16 +721,34 @@ int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, cons
     if (!isfinite(t)) return fail(SFM_E_INVALID_ARG, "t not finite");
     const size_t need = plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes;
     if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-    return run_model(ctx, mw, text, latent, t, v_out, B, T, gh, gw, ws, (hipStream_t)stream);
+    return run_model(ctx, mw, text, latent, t, v_out, B, T, gh, gw, ws, (hipStream_t)stream,
+                     text_lens ? &lens : nullptr);
+}
+}  // namespace
+
+int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent,
+                       float t, float* v_out, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    return model_velocity(ctx, mw, text, nullptr, latent, t, v_out, B, T, gh, gw, ws, ws_bytes, stream);
+}
+
+int sfm_model_velocity_varlen(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                              const int32_t* text_lens, const float* latent, float t, float* v_out, int B, int T,
+                              int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    if (!text_lens) return fail(SFM_E_INVALID_ARG, "text_lens is NULL");
+    return model_velocity(ctx, mw, text, text_lens, latent, t, v_out, B, T, gh, gw, ws, ws_bytes, stream);
 }
 
 namespace {
 
 int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
              const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B, int T, int gh,
-             int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream, LaunchTimer* timer) {
+             int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream, LaunchTimer* timer,
+             const int32_t* text_lens = nullptr) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    TextLens lens;
+    if (text_lens) SFM_CHECK(make_lens(text_lens, B, T, &lens));
+    const TextLens* lp = text_lens ? &lens : nullptr;
     SFM_CHECK(check_model_weights(&ctx->dims, cond));
     SFM_CHECK(check_model_weights(&ctx->dims, uncond));
     if (T > 0) SFM_CHECK(check_ptr(text, "text"));
@@ -688,8 +772,8 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
     const hipStream_t st = (hipStream_t)stream;
     if (timer) {
         // one pass after the other on the caller's stream, so that each timed launch runs alone
-        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, timer));
-        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, timer));
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, lp, timer));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, nullptr, timer));
     } else {
         // the passes are independent: each on its own stream, so that the last, partly filled
         // round of workgroups of one pass's kernels shares the GPU with the other pass
@@ -697,7 +781,7 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
         std::lock_guard<std::mutex> guard(cx->step_lock);
         SFM_TRY_HIP(hipEventRecord(cx->fork, st));
         for (int i = 0; i < 2; ++i) SFM_TRY_HIP(hipStreamWaitEvent(cx->side[i], cx->fork, 0));
-        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, cx->side[0]));
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, cx->side[0], lp));
         SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, cx->side[1]));
         for (int i = 0; i < 2; ++i) {
             SFM_TRY_HIP(hipEventRecord(cx->join[i], cx->side[i]));
@@ -715,6 +799,15 @@ int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sf
                  int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream) {
     return cfg_step(ctx, cond, uncond, text, z, z_out, t, dt, guidance, B, T, gh, gw, v_c_out, v_u_out, ws, ws_bytes,
                     stream, nullptr);
+}
+
+int sfm_cfg_step_varlen(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                        const uint16_t* text, const int32_t* text_lens, const float* z, float* z_out, float t, float dt,
+                        float guidance, int B, int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws,
+                        size_t ws_bytes, void* stream) {
+    if (!text_lens) return fail(SFM_E_INVALID_ARG, "text_lens is NULL");
+    return cfg_step(ctx, cond, uncond, text, z, z_out, t, dt, guidance, B, T, gh, gw, v_c_out, v_u_out, ws, ws_bytes,
+                    stream, nullptr, text_lens);
 }
 
 int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,

@@ -125,6 +125,15 @@ __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 inline int padded_len(int L) { return (int)round_up(L, 128); }
 
+// Per-sample text lengths of a batch whose text prefixes are padded to T rows
+// in memory: sample b's text is rows [0, len[b]) of its prefix, rows
+// [len[b], T) are padding (masked as keys; their own outputs are unspecified)
+// and its image positions start at len[b].  Passed to kernels by value.
+constexpr int kMaxVarlenBatch = 64;
+struct TextLens {
+    int32_t len[kMaxVarlenBatch];
+};
+
 // Records a printf-style message for sfm_last_error (thread-local) and returns code.
 int fail(int code, const char* fmt, ...);
 
@@ -157,13 +166,15 @@ hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const f
                            int K, int L, hipStream_t st);
 
 // k_rope.hip
+// lens: per-sample text lengths (image positions start at len[b]), or NULL when every sample has T
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const uint16_t* kn, const float* cos_t,
                                const float* sin_t, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh,
-                               int gw, int H, float eps, hipStream_t st);
+                               int gw, int H, float eps, const TextLens* lens, hipStream_t st);
 
 // k_attn.hip
+// lens: per-sample text lengths of the T-row text prefixes (keys [len[b], T) masked), or NULL for none
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o, int B, int L,
-                            int H, hipStream_t st);
+                            int H, int T, const TextLens* lens, hipStream_t st);
 
 // k_misc.hip
 hipError_t launch_euler_cfg(const float* z, const float* vc, const float* vu, float* zo, float* vo, int64_t n,

@@ -107,9 +107,13 @@ int sfm_preset_schedule(int preset, int height_px, int width_px, double* t_out, 
     return info.n_steps;
 }
 
-int sfm_sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
-               const uint16_t* text, const float* z, float* z_out, const double* t, const float* guidance,
-               int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+           const uint16_t* text, const int32_t* text_lens, const float* z, float* z_out, const double* t,
+           const float* guidance, int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
     if (n_steps < 1) return sfm::fail(SFM_E_INVALID_ARG, "n_steps < 1");
     if (!t || !guidance) return sfm::fail(SFM_E_INVALID_ARG, "t / guidance is NULL");
     for (int i = 0; i <= n_steps; ++i)
@@ -119,12 +123,36 @@ int sfm_sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_
         if (!(t[i] > t[i + 1])) return sfm::fail(SFM_E_INVALID_ARG, "t not decreasing at %d", i);
     }
     for (int i = 0; i < n_steps; ++i) {
-        const int st = sfm_cfg_step(ctx, cond, uncond, text, i == 0 ? z : z_out, z_out, (float)t[i],
-                                    (float)(t[i] - t[i + 1]), guidance[i], B, T, gh, gw, nullptr, nullptr, ws,
-                                    ws_bytes, stream);
+        const float* zi = i == 0 ? z : z_out;
+        const float ti = (float)t[i], dti = (float)(t[i] - t[i + 1]);
+        const int st = text_lens ? sfm_cfg_step_varlen(ctx, cond, uncond, text, text_lens, zi, z_out, ti, dti,
+                                                       guidance[i], B, T, gh, gw, nullptr, nullptr, ws, ws_bytes,
+                                                       stream)
+                                 : sfm_cfg_step(ctx, cond, uncond, text, zi, z_out, ti, dti, guidance[i], B, T, gh,
+                                                gw, nullptr, nullptr, ws, ws_bytes, stream);
         if (st != SFM_OK) return st;
     }
     return SFM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfm_sample(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+               const uint16_t* text, const float* z, float* z_out, const double* t, const float* guidance,
+               int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
+    return sample(ctx, cond, uncond, text, nullptr, z, z_out, t, guidance, n_steps, B, T, gh, gw, ws, ws_bytes,
+                  stream);
+}
+
+int sfm_sample_varlen(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
+                      const uint16_t* text, const int32_t* text_lens, const float* z, float* z_out, const double* t,
+                      const float* guidance, int n_steps, int B, int T, int gh, int gw, void* ws, size_t ws_bytes,
+                      void* stream) {
+    if (!text_lens) return sfm::fail(SFM_E_INVALID_ARG, "text_lens is NULL");
+    return sample(ctx, cond, uncond, text, text_lens, z, z_out, t, guidance, n_steps, B, T, gh, gw, ws, ws_bytes,
+                  stream);
 }
 
 }  // extern "C"

@@ -101,6 +101,16 @@ SIGNATURES = {
     "sfm_cfg_step_timed": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
                                 _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P),
                                 ctypes.POINTER(_P), _I, ctypes.POINTER(_I)]),
+    "sfm_qk_norm_rope_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P]),
+    "sfm_attention_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "sfm_block_forward_varlen": (_I, [_P, ctypes.POINTER(sfm_block_weights), _P, _P, _P, _I, _I, _P, _I, _I, _P,
+                                      _SZ, _P]),
+    "sfm_model_velocity_varlen": (_I, [_P, ctypes.POINTER(sfm_model_weights), _P, _P, _P, _F, _P, _I, _I, _I, _I,
+                                       _P, _SZ, _P]),
+    "sfm_cfg_step_varlen": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P,
+                                 _P, _P, _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "sfm_sample_varlen": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
+                               _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "sfm_text_project_workspace_bytes": (_SZ, [_I, _I]),
     "sfm_text_project": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _I, _P, _SZ, _P]),
     "sfm_time_grid": (_I, [_I, ctypes.c_double, ctypes.c_double, _I64, _P]),
@@ -300,6 +310,32 @@ def sfm_cfg_step_timed(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z
                                     float(guidance), B, T, gh, gw, _ptr(v_c_out), _ptr(v_u_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream), b, e, n, ctypes.byref(rec)))
     return rec.value
+
+
+def _lens(text_lens):
+    import numpy as np
+    a = np.ascontiguousarray(text_lens, np.int32)
+    return a, a.ctypes.data_as(_P)
+
+
+def sfm_attention_varlen(ctx, q, k, vt, o, B, L, T, text_lens, stream=None):
+    keep, p = _lens(text_lens)
+    _check(lib().sfm_attention_varlen(ctx.handle, _ptr(q), _ptr(k), _ptr(vt), _ptr(o), B, L, T, p, _stream(stream)))
+
+
+def sfm_block_forward_varlen(ctx, w, x_in, x_out, c, B, T, text_lens, gh, gw, ws, stream=None):
+    keep, p = _lens(text_lens)
+    _check(lib().sfm_block_forward_varlen(ctx.handle, ctypes.byref(w.c), _ptr(x_in), _ptr(x_out), _ptr(c), B, T, p,
+                                          gh, gw, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sfm_cfg_step_varlen(ctx, cond, uncond, text, text_lens, z, z_out, t, dt, guidance, B, T, gh, gw, ws,
+                        v_c_out=None, v_u_out=None, stream=None):
+    keep, p = _lens(text_lens)
+    _check(lib().sfm_cfg_step_varlen(ctx.handle, ctypes.byref(cond.c), ctypes.byref(uncond.c), _ptr(text), p,
+                                     _ptr(z), _ptr(z_out), float(t), float(dt), float(guidance), B, T, gh, gw,
+                                     _ptr(v_c_out), _ptr(v_u_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
 
 
 def sfm_text_project(ctx, raw, norm_w, proj, text_out, ws=None, stream=None):

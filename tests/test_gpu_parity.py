@@ -537,6 +537,115 @@ def test_block_deterministic(sfm, ctx_full):
     assert torch.isfinite(a.float()).all()
 
 
+# --------------------------------------------------------------------------- variable text lengths
+
+@pytest.mark.parametrize("B,T,NI,H,lens", [(3, 70, 64, 2, [70, 13, 0]), (2, 128, 200, 2, [0, 64]),
+                                          (2, 512, 4096, 18, [512, 77])])
+def test_attention_varlen(sfm, ctx_tiny, ctx_full, B, T, NI, H, lens):
+    """Per-sample text lengths: each sample's valid rows against attention over
+    its own (unpadded) tokens; padding keys masked or, in whole tiles, skipped."""
+    _say("attention varlen", B, T, NI, lens)
+    ctx = ctx_tiny if H == 2 else ctx_full
+    L = T + NI
+    Lp = sfm.sfm_padded_len(L)
+    q = torch.zeros(B, H, Lp, 256, dtype=torch.bfloat16)
+    k = torch.zeros(B, H, Lp, 256, dtype=torch.bfloat16)
+    vt = torch.zeros(B, H, 256, Lp, dtype=torch.float16)
+    q[:, :, :L] = synth.bf16_normal((B, H, L, 256), ("avq", B, L), 1.0)
+    k[:, :, :L] = synth.bf16_normal((B, H, L, 256), ("avk", B, L), 1.0)
+    vt[:, :, :, :L] = synth.bf16_normal((B, H, 256, L), ("avv", B, L), 1.0).to(torch.float16)
+    o = torch.empty(B * L, H * 256, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_attention_varlen(ctx, q.to(DEV), k.to(DEV), vt[..., vt_order(Lp)].contiguous().to(DEV), o, B, L, T, lens)
+    torch.cuda.synchronize()
+    for b, tb in enumerate(lens):
+        valid = np.r_[0:tb, T:L]
+        qq = np64(q[b][:, valid]).transpose(1, 0, 2)
+        kk = np64(k[b][:, valid]).transpose(1, 0, 2)
+        vv = np64(vt[b][:, :, valid]).transpose(2, 0, 1)
+        sub = np.arange(len(valid)) if len(valid) <= 1000 else np.r_[0:3, tb - 1:tb + 2, len(valid) - 3:len(valid)]
+        sub = sub[(sub >= 0) & (sub < len(valid))]
+        ref = N.bf16_round(O.attention(qq, kk, vv, rows=sub)).reshape(len(sub), -1)
+        got = np64(o[b * L + valid[sub]])
+        assert rel_l2(got, ref) < 5e-3
+
+
+def test_block_varlen_tiny(sfm, ctx_tiny):
+    """Three prompts of 16, 5 and 0 text tokens padded to 16: every sample's
+    text and image rows against the sample computed alone."""
+    _say("block varlen tiny")
+    w = synth.Workload("tiny_vl", synth.TINY, 3, 16, 16, 16)
+    lens = [16, 5, 0]
+    p = synth.block_params(w.shape, (0, w.name), "fp8")
+    x, c = synth.block_inputs(w)
+    bw = sfm.BlockWeights(to_device(p))
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx_tiny, 3, w.T, w.gh, w.gw, bw.fmt))
+    xo = torch.empty_like(x, device=DEV)
+    sfm.sfm_block_forward_varlen(ctx_tiny, bw, x.to(DEV), xo, c.to(DEV), 3, w.T, lens, w.gh, w.gw, ws)
+    torch.cuda.synchronize()
+    ref = O.block_forward_varlen(np64(x), c.numpy().astype(np.float64), oracle_block(p), w.T, lens, w.gh, w.gw,
+                                 O.TINY)
+    got = np64(xo)
+    assert np.isfinite(got).all()
+    ok = ~np.isnan(ref)
+    assert rel_l2(got[ok], ref[ok]) < 1e-2
+    xin = np64(x)
+    assert rel_l2(got[ok] - xin[ok], ref[ok] - xin[ok]) < UPDATE_BAR["fp8"]
+
+
+def test_block_varlen_full_sampled(sfm, ctx_full):
+    """1024^2 block with two prompts (512 and 77 text tokens, padded to 512):
+    sampled rows of the short prompt against that prompt computed alone, and
+    the full-length prompt against the uniform call."""
+    _say("block varlen full")
+    w = synth.Workload("full_vl", synth.FULL, 2, 512, 64, 64)
+    lens = [512, 77]
+    p = synth.block_params(w.shape, (0, w.name), "fp8")
+    x, c = synth.block_inputs(w)
+    bw = sfm.BlockWeights(to_device(p))
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx_full, 2, w.T, w.gh, w.gw, bw.fmt))
+    xo = torch.empty_like(x, device=DEV)
+    xu = torch.empty_like(x, device=DEV)
+    xd, cd = x.to(DEV), c.to(DEV)
+    sfm.sfm_block_forward_varlen(ctx_full, bw, xd, xo, cd, 2, w.T, lens, w.gh, w.gw, ws)
+    sfm.sfm_block_forward(ctx_full, bw, xd, xu, cd, 2, w.T, w.gh, w.gw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xo[0], xu[0])          # a full-length prompt is unaffected
+    valid = np.r_[0:77, 512:w.L]
+    xs = np64(x[1])[valid][None]
+    sub = np.array([0, 40, 76, 77, 78, 1000, 2047, 4172])
+    ref = O.block_forward(xs, c[1:2].numpy().astype(np.float64), oracle_block(p), 77, w.gh, w.gw, O.IDEOGRAM4,
+                          rows=sub)
+    got = np64(xo[1])[valid[sub]]
+    xin = xs[0][sub]
+    assert rel_l2(got, ref) < 1e-2
+    assert rel_l2(got - xin, ref - xin) < UPDATE_BAR["fp8"]
+
+
+def test_cfg_step_varlen_tiny(sfm, ctx_tiny):
+    """Two prompts (16 and 7 text tokens) through a 2-layer guided step: the
+    velocities of each sample against the oracle's per-sample step."""
+    _say("cfg step varlen tiny")
+    w = synth.Workload("tiny_svl", synth.TINY, 2, 16, 16, 16, layers=2)
+    lens = [16, 7]
+    cond = synth.model_params(w.shape, 2, (0, "tiny_vc"))
+    unc = synth.model_params(w.shape, 2, (0, "tiny_vu"))
+    text, z, t, dt = synth.step_inputs(w)
+    cm, um = sfm.ModelWeights(to_device(cond)), sfm.ModelWeights(to_device(unc))
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 2, w.T, w.gh, w.gw))
+    vc = torch.empty(2, 256, 128, device=DEV)
+    vu = torch.empty_like(vc)
+    zo = torch.empty_like(vc)
+    sfm.sfm_cfg_step_varlen(ctx_tiny, cm, um, text.to(DEV), lens, z.to(DEV), zo, t, dt, 4.0, 2, w.T, w.gh, w.gw, ws,
+                            vc, vu)
+    torch.cuda.synchronize()
+    z2, v, rvc, rvu = O.cfg_step_varlen(np64(text), lens, np64(z), [t, t], dt, 4.0, oracle_model(cond),
+                                        oracle_model(unc), w.gh, w.gw, O.TINY)
+    for b in range(2):
+        assert rel_l2(vc[b].cpu().numpy(), rvc[b]) < 3e-2
+    assert rel_l2(vu.cpu().numpy(), rvu) < 3e-2
+    assert rel_l2(zo.cpu().numpy() - np64(z), z2 - np64(z)) < 3e-2
+
+
 # --------------------------------------------------------------------------- model + CFG step
 
 def test_cfg_step_tiny_34_layers(sfm, ctx_tiny):
