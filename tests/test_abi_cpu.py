@@ -195,20 +195,18 @@ def test_text_project_argument_checks(S):
 
 
 def test_varlen_argument_checks(S):
-    """Per-sample text lengths are checked on the host: NULL, out of [0, T],
-    more than 64 samples."""
+    """The _varlen calls refuse a NULL length array before anything else (the
+    range checks need a context, so they run on the GPU side of the tests)."""
     L = S.lib()
     P = ctypes.c_void_p
     good = P(1 << 20)
-    ok = np.array([3, 0], np.int32)
-    bad = np.array([3, 5], np.int32)
-    assert L.sfm_attention_varlen(None, good, good, good, good, 2, 100, 4, ok.ctypes.data_as(P), None) == -1
-    d = L.sfm_dims_ideogram4()
-    # a fake context pointer is never dereferenced before the length checks fail: use the NULL-ctx path instead
-    assert L.sfm_block_forward_varlen(None, None, good, good, good, 2, 4, None, 16, 16, good, 0, None) == -1
-    assert L.sfm_cfg_step_varlen(None, None, None, good, None, good, good, 0.5, 0.1, 4.0, 2, 4, 16, 16, None, None,
-                                 good, 0, None) == -1
-    assert L.sfm_model_velocity_varlen(None, None, good, None, good, 0.5, good, 2, 4, 16, 16, good, 0, None) == -1
-    assert L.sfm_sample_varlen(None, None, None, good, None, good, good, None, None, 1, 2, 4, 16, 16, good, 0,
-                               None) == -1
-    del d, bad
+    assert L.sfm_block_forward_varlen(good, None, good, good, good, 2, 4, None, 16, 16, good, 1 << 30, None) == -1
+    assert L.sfm_cfg_step_varlen(good, None, None, good, None, good, good, 0.5, 0.1, 4.0, 2, 4, 16, 16, None, None,
+                                 good, 1 << 30, None) == -1
+    assert L.sfm_model_velocity_varlen(good, None, good, None, good, 0.5, good, 2, 4, 16, 16, good, 1 << 30,
+                                       None) == -1
+    assert b"text_lens" in L.sfm_last_error()
+    t = np.array([1.0, 0.0])
+    g = np.array([4.0], np.float32)
+    assert L.sfm_sample_varlen(good, None, None, good, None, good, good, t.ctypes.data_as(P), g.ctypes.data_as(P), 1,
+                               2, 4, 16, 16, good, 1 << 30, None) == -1
