@@ -136,6 +136,25 @@ def block_bench(sfm, synth, ctx, name, iters=5):
             "weights": w.wfmt}
 
 
+def block_varlen_bench(sfm, synth, ctx, lens=(512, 77), iters=5):
+    """Two 1024^2 prompts of different text lengths in one batch (text padded
+    to 512 rows): the block with per-sample lengths.  Tokens counted are the
+    real ones (text + image of each sample)."""
+    import torch
+    w = synth.Workload("block_1024_varlen", synth.FULL, len(lens), 512, 64, 64)
+    p = synth.block_params(w.shape, (0, w.name), "fp8", device="cuda")
+    bw = sfm.BlockWeights(p)
+    x, c = synth.block_inputs(w, device="cuda")
+    xo = torch.empty_like(x)
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw, bw.fmt))
+    sec = time_gpu(lambda: sfm.sfm_block_forward_varlen(ctx, bw, x, xo, c, w.B, w.T, list(lens), w.gh, w.gw, ws),
+                   iters)
+    real = sum(t + w.gh * w.gw for t in lens)
+    fl = sum(block_flops(t + w.gh * w.gw, 1) for t in lens)
+    return {"workload": f"batch of {len(lens)} at 1024^2 with text lengths {list(lens)} padded to 512",
+            "ms": round(sec * 1e3, 4), "tokens_per_s": round(real / sec, 1), "tflops": round(fl / sec / 1e12, 2)}
+
+
 def text_project_bench(sfm, synth, ctx, M=512, iters=10):
     """The text-conditioning projection of one 512-token prompt: 53,248 raw
     features per token to 4608 (RMSNorm + E4M3 + FP8 GEMM, K 53,248)."""
@@ -397,6 +416,7 @@ def main():
         for name in ("block_1024", "block_2048", "block_6to1_nf4"):
             extra[name] = block_bench(sfm, synth, ctx, name)
         extra["text_projection_512"] = text_project_bench(sfm, synth, ctx)
+        extra["block_1024_varlen_b2"] = block_varlen_bench(sfm, synth, ctx)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample)
 
     line = {
