@@ -115,9 +115,42 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
         el = time.perf_counter() - t0
         samples[name] = {"steps": len(g), "s_per_image": round(el, 4), "ms_per_step": round(el / len(g) * 1e3, 3),
                          "finite": bool(torch.isfinite(zo).all())}
+    streamed = streamed_bench(sfm, ctx, cond, cm, text, z, t, w) if presets else None
     del cond, unc, cm, um, ws
     torch.cuda.empty_cache()
-    return sec, ok, launches[:w.layers], launches[w.layers:], samples
+    return sec, ok, launches[:w.layers], launches[w.layers:], samples, streamed
+
+
+def streamed_bench(sfm, ctx, cond, cm, text, z, t, w, iters=2):
+    """The conditional velocity pass (34 layers, 1024^2) with its block weights
+    in pinned host memory, streamed layer by layer, against the same pass with
+    resident weights.  H2D rate = block weight bytes copied per second."""
+    import dataclasses
+    import torch
+
+    def pin(o):
+        if isinstance(o, torch.Tensor):
+            return o.cpu().pin_memory()
+        if isinstance(o, tuple):
+            return tuple(pin(x) for x in o)
+        if dataclasses.is_dataclass(o):
+            return dataclasses.replace(o, **{f.name: pin(getattr(o, f.name)) for f in dataclasses.fields(o)})
+        return o
+
+    host = dataclasses.replace(cond, blocks=[pin(b) for b in cond.blocks])
+    mh = sfm.ModelWeights(host)
+    v = torch.empty(w.B, w.gh * w.gw, w.shape.latent_ch, device="cuda")
+    ws_s = sfm.workspace(sfm.lib().sfm_streamed_workspace_bytes(ctx.handle, w.B, w.T, w.gh, w.gw))
+    ws_r = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw))
+    s_str = time_gpu(lambda: sfm.sfm_model_velocity_streamed(ctx, mh, text, z, t, v, w.B, w.T, w.gh, w.gw, ws_s),
+                     iters)
+    s_res = time_gpu(lambda: sfm.sfm_model_velocity(ctx, cm, text, z, t, v, w.B, w.T, w.gh, w.gw, ws_r), iters)
+    blk = sum(x.numel() * x.element_size() for b in host.blocks
+              for x in (b.qkv + b.o + b.gate_up + b.down + (b.q_norm, b.k_norm, b.mod_w, b.mod_b)))
+    del host, mh, ws_s, ws_r
+    return {"workload": "conditional pass, 34 layers at 1024^2, block weights in pinned host memory",
+            "ms_streamed": round(s_str * 1e3, 2), "ms_resident": round(s_res * 1e3, 2),
+            "block_weight_bytes": blk, "h2d_gb_s": round(blk / s_str / 1e9, 2)}
 
 
 def block_bench(sfm, synth, ctx, name, iters=5):
@@ -406,7 +439,7 @@ def main():
     w = synth.WORKLOADS["cfg_step_1024"]
     presets = () if args.no_extra else (("V4_TURBO_12", sfm.SFM_PRESET_V4_TURBO_12),
                                          ("V4_QUALITY_48", sfm.SFM_PRESET_V4_QUALITY_48))
-    sec, ok, gu_cond, gu_uncond, samples = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup, presets)
+    sec, ok, gu_cond, gu_uncond, samples, streamed = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup, presets)
     tokens = w.layers * (w.B * (w.T + w.gh * w.gw) + w.B * w.gh * w.gw)
     flops = w.layers * (block_flops(w.T + w.gh * w.gw, w.B) + block_flops(w.gh * w.gw, w.B))
     step_tflops = flops / sec / 1e12
@@ -443,6 +476,7 @@ def main():
         "cpu_baseline": cpu,
         "blocks": extra,
         "sampler_1024": samples,
+        "streamed_weights_1024": streamed,
     }
     print(json.dumps(line))
 

@@ -279,7 +279,28 @@ int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, co
                        int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,
                        void* const* ev_begin, void* const* ev_end, int n_events, int* n_recorded);
 
-/* ---------------------------------------------------------------- variable text lengths */
+/* ---------------------------------------------------------------- host-streamed weights */
+
+/* Workspace bytes of sfm_model_velocity_streamed: a velocity-model workspace
+ * plus two device slots for one block's FP8 weights each (~274 MB at the spec
+ * dims). */
+size_t sfm_streamed_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw);
+
+/* sfm_model_velocity with the blocks' weights in host memory (SimpleTuner
+ * Ideogram 4 quick start, "Validation": the unconditional transformer can be
+ * kept in CPU memory and its layers streamed to the accelerator on every
+ * forward pass, trading speed for device memory).  Every pointer of
+ * mw->blocks[i] points to host memory, pinned (hipHostMalloc) for the copies
+ * to overlap the computation; the other weights of mw are device memory.
+ * Block i + 1's weights are copied into one of two workspace slots on a
+ * context-owned copy stream while block i computes from the other; results
+ * equal sfm_model_velocity's bitwise.  Calls on one context are serialised.
+ * Errors as sfm_model_velocity. */
+int sfm_model_velocity_streamed(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                                const float* latent, float t, float* v_out, int B, int T, int gh, int gw, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- variable text lengths *//* ---------------------------------------------------------------- variable text lengths */
 
 /* Batches of prompts with different text lengths.  The text prefixes are
  * padded to T rows in memory ([B][T + gh*gw][D] as everywhere); text_lens is

@@ -306,6 +306,54 @@ int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
     return SFM_OK;
 }
 
+// One block's FP8 weights laid out in a device slot of the streamed-weights
+// ring (256-byte aligned pieces); fills *w with pointers into base (sizes only
+// when base is NULL) and returns the slot's bytes.
+size_t plan_slot(const sfm_dims* d, char* base, sfm_block_weights* w) {
+    const int64_t D = d->emb_dim, F = d->intermediate, A = d->adaln_dim;
+    Carve c(base);
+    auto qw = [&](int64_t n, int64_t k) {
+        sfm_qweight q;
+        q.fmt = SFM_W_FP8_E4M3;
+        q.n = (int32_t)n;
+        q.k = (int32_t)k;
+        q.q = c.take<uint8_t>((size_t)(n * k));
+        q.scale = c.take<float>((size_t)n);
+        return q;
+    };
+    w->qkv = qw(3 * D, D);
+    w->o = qw(D, D);
+    w->gate_up = qw(2 * F, D);
+    w->down = qw(D, F);
+    w->q_norm = c.take<uint16_t>(256);
+    w->k_norm = c.take<uint16_t>(256);
+    w->mod_w = c.take<uint16_t>((size_t)(4 * D * A));
+    w->mod_b = c.take<float>((size_t)(4 * D));
+    return c.off;
+}
+
+// Enqueue the copies of block weights `src` (host memory) into the slot `dst` on stream st.
+hipError_t stage_block(const sfm_dims* d, const sfm_block_weights* src, const sfm_block_weights* dst, hipStream_t st) {
+    const int64_t D = d->emb_dim, F = d->intermediate, A = d->adaln_dim;
+    struct Piece {
+        const void* dst;
+        const void* src;
+        size_t bytes;
+    } pieces[] = {
+        {dst->qkv.q, src->qkv.q, (size_t)(3 * D * D)},        {dst->qkv.scale, src->qkv.scale, (size_t)(3 * D * 4)},
+        {dst->o.q, src->o.q, (size_t)(D * D)},                {dst->o.scale, src->o.scale, (size_t)(D * 4)},
+        {dst->gate_up.q, src->gate_up.q, (size_t)(2 * F * D)}, {dst->gate_up.scale, src->gate_up.scale, (size_t)(2 * F * 4)},
+        {dst->down.q, src->down.q, (size_t)(D * F)},          {dst->down.scale, src->down.scale, (size_t)(D * 4)},
+        {dst->q_norm, src->q_norm, 512},                      {dst->k_norm, src->k_norm, 512},
+        {dst->mod_w, src->mod_w, (size_t)(4 * D * A * 2)},    {dst->mod_b, src->mod_b, (size_t)(4 * D * 4)},
+    };
+    for (const Piece& p : pieces) {
+        const hipError_t e = hipMemcpyAsync(const_cast<void*>(p.dst), p.src, p.bytes, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Per-sample text lengths from the caller's host array: B <= kMaxVarlenBatch, 0 <= len <= T.
 int make_lens(const int32_t* text_lens, int B, int T, TextLens* out) {
     if (!text_lens) return fail(SFM_E_INVALID_ARG, "text_lens is NULL");
@@ -336,6 +384,58 @@ int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_
     SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
     SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
                                    B * N, C, D, st));
+    return SFM_OK;
+}
+
+// The velocity model with its blocks' weights in host memory: block i + 1 is
+// copied into ring slot (i + 1) & 1 on the context's copy stream while block i
+// computes from slot i & 1 on `st`; a slot is refilled only after the block
+// that read it has finished (consumed event), and a block starts only after
+// its slot is filled (copied event).
+int run_model_streamed(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                       const float* latent, float t, float* v_out, int B, int T, int gh, int gw, void* ws,
+                       hipStream_t st) {
+    sfm_context* cx = const_cast<sfm_context*>(ctx);
+    const sfm_dims* d = &ctx->dims;
+    const int N = gh * gw, L = T + N, D = d->emb_dim, A = d->adaln_dim, C = d->latent_ch;
+    Carve c(ws);
+    char* model_ws = c.take<char>(plan_model(d, B, T, gh, gw, nullptr).bytes);
+    sfm_block_weights slot[2];
+    const size_t slot_bytes = plan_slot(d, nullptr, &slot[0]);
+    for (int s = 0; s < 2; ++s) plan_slot(d, c.take<char>(slot_bytes), &slot[s]);
+    StepWs w = plan_model(d, B, T, gh, gw, model_ws);
+    const int n = mw->num_layers;
+    std::lock_guard<std::mutex> guard(cx->step_lock);
+    // the ring may still be read by earlier work on st: the copies start after it
+    SFM_TRY_HIP(hipEventRecord(cx->done, st));
+    SFM_TRY_HIP(hipStreamWaitEvent(cx->copy, cx->done, 0));
+    if (n > 0) {
+        SFM_LAUNCH(stage_block(d, &mw->blocks[0], &slot[0], cx->copy));
+        SFM_TRY_HIP(hipEventRecord(cx->copied[0], cx->copy));
+    }
+    SFM_LAUNCH(launch_timestep_embed(t, w.e, B, A, st));
+    SFM_LAUNCH(launch_gemv(w.e, 0, mw->t_w1, mw->t_b1, w.hdn, B, A, A, st));
+    SFM_LAUNCH(launch_gemv(w.hdn, 1, mw->t_w2, mw->t_b2, w.c, B, A, A, st));
+    if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
+    SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
+    for (int i = 0; i < n; ++i) {
+        const int s = i & 1, s1 = (i + 1) & 1;
+        if (i + 1 < n) {
+            if (i >= 1) SFM_TRY_HIP(hipStreamWaitEvent(cx->copy, cx->consumed[s1], 0));
+            SFM_LAUNCH(stage_block(d, &mw->blocks[i + 1], &slot[s1], cx->copy));
+            SFM_TRY_HIP(hipEventRecord(cx->copied[s1], cx->copy));
+        }
+        SFM_TRY_HIP(hipStreamWaitEvent(st, cx->copied[s], 0));
+        SFM_CHECK(run_block(ctx, &slot[s], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st));
+        SFM_TRY_HIP(hipEventRecord(cx->consumed[s], st));
+    }
+    SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
+    SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
+    SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
+                                   B * N, C, D, st));
+    // later work on the copy stream (the next call's first copy) follows this call's blocks
+    SFM_TRY_HIP(hipEventRecord(cx->done, st));
+    SFM_TRY_HIP(hipStreamWaitEvent(cx->copy, cx->done, 0));
     return SFM_OK;
 }
 
@@ -440,6 +540,12 @@ int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out) {
     for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipStreamCreateWithFlags(&ctx->side[i], hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->fork, hipEventDisableTiming);
     for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&ctx->join[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+        e = hipEventCreateWithFlags(&ctx->copied[i], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->consumed[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming);
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         sfm_context_destroy(ctx);
@@ -456,8 +562,12 @@ void sfm_context_destroy(sfm_context* ctx) {
     for (int i = 0; i < 2; ++i) {
         if (ctx->side[i]) (void)hipStreamDestroy(ctx->side[i]);
         if (ctx->join[i]) (void)hipEventDestroy(ctx->join[i]);
+        if (ctx->copied[i]) (void)hipEventDestroy(ctx->copied[i]);
+        if (ctx->consumed[i]) (void)hipEventDestroy(ctx->consumed[i]);
     }
     if (ctx->fork) (void)hipEventDestroy(ctx->fork);
+    if (ctx->copy) (void)hipStreamDestroy(ctx->copy);
+    if (ctx->done) (void)hipEventDestroy(ctx->done);
     delete ctx;
 }
 
@@ -729,6 +839,33 @@ int model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const ui
 int sfm_model_velocity(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent,
                        float t, float* v_out, int B, int T, int gh, int gw, void* ws, size_t ws_bytes, void* stream) {
     return model_velocity(ctx, mw, text, nullptr, latent, t, v_out, B, T, gh, gw, ws, ws_bytes, stream);
+}
+
+size_t sfm_streamed_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw) {
+    if (!ctx) return 0;
+    Carve c(nullptr);
+    c.take<char>(plan_model(&ctx->dims, B, T, gh, gw, nullptr).bytes);
+    sfm_block_weights tmp;
+    const size_t slot = plan_slot(&ctx->dims, nullptr, &tmp);
+    c.take<char>(slot);
+    c.take<char>(slot);
+    return c.off + 256;
+}
+
+int sfm_model_velocity_streamed(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,
+                                const float* latent, float t, float* v_out, int B, int T, int gh, int gw, void* ws,
+                                size_t ws_bytes, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    SFM_CHECK(check_model_weights(&ctx->dims, mw));
+    if (T > 0) SFM_CHECK(check_ptr(text, "text"));
+    SFM_CHECK(check_ptr(latent, "latent"));
+    SFM_CHECK(check_ptr(v_out, "v_out"));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    if (!isfinite(t)) return fail(SFM_E_INVALID_ARG, "t not finite");
+    const size_t need = sfm_streamed_workspace_bytes(ctx, B, T, gh, gw);
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return run_model_streamed(ctx, mw, text, latent, t, v_out, B, T, gh, gw, ws, (hipStream_t)stream);
 }
 
 int sfm_model_velocity_varlen(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text,

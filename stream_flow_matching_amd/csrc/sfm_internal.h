@@ -22,6 +22,12 @@ struct sfm_context {
     hipStream_t side[2] = {nullptr, nullptr};
     hipEvent_t fork = nullptr;
     hipEvent_t join[2] = {nullptr, nullptr};
+    // host-streamed block weights: layer copies run on `copy` into two device
+    // slots; copied[s] marks slot s filled, consumed[s] its block computed
+    hipStream_t copy = nullptr;
+    hipEvent_t copied[2] = {nullptr, nullptr};
+    hipEvent_t consumed[2] = {nullptr, nullptr};
+    hipEvent_t done = nullptr;
     std::mutex step_lock;
 };
 

@@ -101,6 +101,9 @@ SIGNATURES = {
     "sfm_cfg_step_timed": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
                                 _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P, ctypes.POINTER(_P),
                                 ctypes.POINTER(_P), _I, ctypes.POINTER(_I)]),
+    "sfm_streamed_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I]),
+    "sfm_model_velocity_streamed": (_I, [_P, ctypes.POINTER(sfm_model_weights), _P, _P, _F, _P, _I, _I, _I, _I, _P,
+                                         _SZ, _P]),
     "sfm_qk_norm_rope_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _P]),
     "sfm_attention_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P]),
     "sfm_block_forward_varlen": (_I, [_P, ctypes.POINTER(sfm_block_weights), _P, _P, _P, _I, _I, _P, _I, _I, _P,
@@ -316,6 +319,13 @@ def _lens(text_lens):
     import numpy as np
     a = np.ascontiguousarray(text_lens, np.int32)
     return a, a.ctypes.data_as(_P)
+
+
+def sfm_model_velocity_streamed(ctx, mw: ModelWeights, text, latent, t, v_out, B, T, gh, gw, ws, stream=None):
+    """Velocity with mw's block weights in (pinned) host memory, streamed per layer."""
+    _check(lib().sfm_model_velocity_streamed(ctx.handle, ctypes.byref(mw.c), _ptr(text) if T > 0 else None,
+                                             _ptr(latent), float(t), _ptr(v_out), B, T, gh, gw, _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def sfm_attention_varlen(ctx, q, k, vt, o, B, L, T, text_lens, stream=None):

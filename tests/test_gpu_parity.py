@@ -743,6 +743,53 @@ def test_sample_tiny_against_oracle_sampler(sfm, ctx_tiny):
     assert rel_l2(zo.cpu().numpy() - np64(z), ref - np64(z)) < 3e-2
 
 
+def _pinned(obj):
+    """Copy of a synth dataclass with every tensor in pinned host memory."""
+    import dataclasses
+    if isinstance(obj, torch.Tensor):
+        return obj.cpu().contiguous().pin_memory()
+    if isinstance(obj, tuple):
+        return tuple(_pinned(x) for x in obj)
+    if dataclasses.is_dataclass(obj):
+        return dataclasses.replace(obj, **{f.name: _pinned(getattr(obj, f.name)) for f in dataclasses.fields(obj)})
+    return obj
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_model_velocity_streamed_equals_resident(sfm, ctx_tiny, ctx_full, full):
+    """Block weights in pinned host memory, copied layer by layer into a
+    two-slot device ring while the previous layer computes: the velocity equals
+    the resident-weight call bitwise, on two calls in a row (the second reuses
+    the ring) with different inputs."""
+    _say("velocity streamed", full)
+    ctx = ctx_full if full else ctx_tiny
+    w = synth.Workload("str_full" if full else "str_tiny", synth.FULL if full else synth.TINY, 1, 64 if full else 16,
+                       32 if full else 16, 32 if full else 16, layers=3 if full else 5)
+    mp = synth.model_params(w.shape, w.layers, (0, w.name))
+    dev = to_device(mp)
+    host = dataclasses_replace_blocks(dev, [_pinned(b) for b in mp.blocks])
+    mw_dev, mw_host = sfm.ModelWeights(dev), sfm.ModelWeights(host)
+    text, z, t, _ = synth.step_inputs(w)
+    C = 128
+    ws_r = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx, 1, w.T, w.gh, w.gw))
+    ws_s = sfm.workspace(sfm.lib().sfm_streamed_workspace_bytes(ctx.handle, 1, w.T, w.gh, w.gw))
+    for rep in range(2):
+        zz = (z * (1.0 + rep)).to(DEV)
+        tt = t * (0.5 + 0.25 * rep)
+        v_r = torch.empty(1, w.gh * w.gw, C, device=DEV)
+        v_s = torch.empty_like(v_r)
+        sfm.sfm_model_velocity(ctx, mw_dev, text.to(DEV), zz, tt, v_r, 1, w.T, w.gh, w.gw, ws_r)
+        sfm.sfm_model_velocity_streamed(ctx, mw_host, text.to(DEV), zz, tt, v_s, 1, w.T, w.gh, w.gw, ws_s)
+        torch.cuda.synchronize()
+        assert torch.isfinite(v_s).all()
+        assert torch.equal(v_r, v_s)
+
+
+def dataclasses_replace_blocks(p, blocks):
+    import dataclasses
+    return dataclasses.replace(p, blocks=blocks)
+
+
 def test_cfg_step_full_properties(sfm, ctx_full):
     """The 34-layer, two-weight-set step at 1024^2 (the timed workload):
     finite, deterministic, and z' = z + dt (v_u + 4 (v_c - v_u)) holds for the
