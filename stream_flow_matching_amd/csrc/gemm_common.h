@@ -188,8 +188,9 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 //     latency overlaps them, then added on the way out (one bf16 rounding).
 // Scales come from LDS, where the kernel put them before its main loop: rsl
 // = row scales of the wave's rows, csl = scales of the wave's B-tile columns,
-// gl = gate rows of batches bt0, bt0 + 1, bt0 + 2 (stride BN floats, offset to
-// the wave's columns; RESID only).  The gate row of token row m is batch m / L
+// gl = gate rows times column scales, gate[b][n] * sw[n], of batches bt0,
+// bt0 + 1, bt0 + 2 (stride BN floats, offset to the wave's columns; RESID
+// only), so that gate * y = (acc * sa) * gl.  The gate row of token row m is batch m / L
 // and a wave's rows touch at most two batches (L >= TM).  lds: the wave's
 // staging region (at least TM * TN * 2 bytes; the RESID padding needs
 // TM / 2 * (TN * 4 + 16)).
@@ -215,13 +216,21 @@ __device__ __forceinline__ void gemm_epilogue_lds_t(const v16f (&acc)[FM][FN], u
         auto swz = [](int ch, int row) { return ch ^ ((row / (16 / NCH)) & (NCH - 1)); };
         const int64_t ld_out = SW ? N / 2 : N;
         const int64_t col0 = SW ? (int64_t)tn * (BN / 2) + wn * (TN / 2) : (int64_t)tn * BN + wn * TN;
+        constexpr int NJ = SW ? FN / 2 : FN;
 #pragma unroll
-        for (int j = 0; j < (SW ? FN / 2 : FN); ++j) {
+        for (int j = 0; j < NJ; ++j) {
+            // the column scales of the four groups first (one wait instead of one per group)
+            v4f cgs[4], cus[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cgs[q] = colscale(32 * j + 8 * q + 4 * lg);
+                if constexpr (SW) cus[q] = colscale(32 * j + 8 * q + 4 * lg + TN / 2);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = 32 * j + 8 * q + 4 * lg;
-                const v4f cg = colscale(c);
-                const v4f cu = SW ? colscale(c + TN / 2) : cg;
+                const v4f cg = cgs[q];
+                const v4f cu = SW ? cus[q] : cg;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     float y[4];
@@ -271,20 +280,25 @@ __device__ __forceinline__ void gemm_epilogue_lds_t(const v16f (&acc)[FM][FN], u
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
+                // gate * column scale of the first and the last batch of the wave's rows
+                v4f g0[4], g1[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = 32 * j + 8 * q + 4 * lg;
-                    const v4f cs = colscale(c);
-                    const v4f g0 = *reinterpret_cast<const v4f*>(gl + (b_first - bt0) * BN + c);
-                    const v4f g1 = *reinterpret_cast<const v4f*>(gl + (b_last - bt0) * BN + c);
+                    g0[q] = *reinterpret_cast<const v4f*>(gl + (b_first - bt0) * BN + c);
+                    g1[q] = *reinterpret_cast<const v4f*>(gl + (b_last - bt0) * BN + c);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 32 * j + 8 * q + 4 * lg;
 #pragma unroll
                     for (int ii = 0; ii < FM / 2; ++ii) {
                         const int i = p * (FM / 2) + ii;
                         const int row = 32 * ii + lc;  // row inside the pass
-                        const v4f g = m0w + 32 * i + lc < row_split ? g0 : g1;
+                        const v4f g = m0w + 32 * i + lc < row_split ? g0[q] : g1[q];
                         v4f v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = g[e] * (acc[i][j][4 * q + e] * rs[i] * cs[e]);
+                        for (int e = 0; e < 4; ++e) v[e] = (acc[i][j][4 * q + e] * rs[i]) * g[e];
                         *reinterpret_cast<v4f*>(lds + row * PITCH + (swz(c >> 2, row) << 4)) = v;
                     }
                 }

@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     // the epilogue's scales go to LDS behind the ring: row scales [BM], column scales [BN] and,
-    // for the gated residual, the gate rows of the (at most three) batches the tile's rows touch
-    // [3][BN]; their loads are issued before the first stages' and land under them
+    // for the gated residual, gate * column scale for the (at most three) batches the tile's rows
+    // touch [3][BN]; their loads are issued before the first stages' and land under them
     constexpr int NSC = BM + (EPI == SFM_EPI_RESID_GATE ? 4 : 1) * BN;
     constexpr int NSL = (NSC + 255) / 256;
     float* scl = reinterpret_cast<float*>(smem + 2 * STAGE);
@@ -189,6 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         } else if (e < NSC) {
             const int g = (e - BM - BN) / BN, c = (e - BM - BN) % BN;
             v = gate[(int64_t)min(bt0 + g, (M - 1) / L) * gate_stride + (int64_t)tn * BN + c];
+            if (sw) v *= sw[weight_row<EPI, BN, TN>(c, tn, N)];
         }
         scv[k] = v;
     }
