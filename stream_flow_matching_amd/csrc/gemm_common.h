@@ -40,137 +40,6 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 }
 
 // Epilogue of a wave's TM x TN tile of 32x32 accumulators (TM = 32 FM,
-// TN = 32 FN), staged through the wave's own LDS region so that global stores
-// are whole 16-byte row chunks.  Element r of acc[i][j] in lane l is tile row
-// 32 i + 8 (r >> 2) + 4 (l >> 5) + (r & 3) and B-tile column 32 j + (l & 31).
-//   STORE / SWIGLU: the final bf16 values are written to LDS (row-major, 16-byte
-//     chunks XOR-swizzled by row so that the two half-waves of a write, four rows
-//     apart, and the 16 lanes of a read hit distinct banks), then each lane reads
-//     16-byte chunks back and stores them.
-//   RESID_GATE: gate * y is staged in fp32 (64 rows at a time), read back four
-//     columns per lane and added to the residual there, so the bf16 rounding of
-//     resid + gate * y happens once, as in the direct form.
-// Scales: sa[row] per token row, sw[weight row] per B-tile column (1 when the
-// pointer is null: operands that carry no scale); the gate row
-// of a token row is its batch m / L, and the wave's rows touch at most two
-// batches (callers guarantee L >= TM).  Rows past M are computed from the
-// clamped operand rows and not stored.  lds: 128 * TN * 2 bytes per wave
-// (32 KiB for TN = 128), 16-byte aligned.
-template <int EPI, int BN, int TN, int FM, int FN>
-__device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uint8_t* lds, int m0w, int wn, int tn,
-                                                  int lane, int M, int N, int L, uint16_t* out, const uint16_t* resid,
-                                                  const float* gate, int64_t gate_stride, const float* sa,
-                                                  const float* sw) {
-    constexpr int TM = 32 * FM;
-    const int lc = lane & 31, lg = lane >> 5;
-    float rsv[FM][16];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            rsv[i][r] = sa ? sa[min(m0w + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3), M - 1)] : 1.0f;
-    float cs[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) cs[j] = sw ? sw[weight_row<EPI, BN, TN>(wn * TN + 32 * j + lc, tn, N)] : 1.0f;
-
-    if constexpr (EPI == SFM_EPI_STORE || EPI == SFM_EPI_SWIGLU) {
-        constexpr int OC = EPI == SFM_EPI_SWIGLU ? TN / 2 : TN;  // output columns of the wave tile
-        constexpr int NCH = OC / 8;                                // 16-byte chunks per LDS row
-        const int ld_out = EPI == SFM_EPI_SWIGLU ? N / 2 : N;
-        const int64_t col0 = EPI == SFM_EPI_SWIGLU ? (int64_t)tn * (BN / 2) + wn * (TN / 2) : (int64_t)tn * BN + wn * TN;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < (EPI == SFM_EPI_SWIGLU ? FN / 2 : FN); ++j) {
-                const int c = 32 * j + lc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-                    float y;
-                    if constexpr (EPI == SFM_EPI_SWIGLU)
-                        y = swiglu_fast(acc[i][j][r] * rsv[i][r] * cs[j], acc[i][j + FN / 2][r] * rsv[i][r] * cs[j + FN / 2]);
-                    else
-                        y = acc[i][j][r] * rsv[i][r] * cs[j];
-                    const int off = row * (OC * 2) + (((c >> 3) ^ (row & (NCH - 1))) << 4) + (c & 7) * 2;
-                    *reinterpret_cast<uint16_t*>(lds + off) = (uint16_t)cvt_bf16x2(y, 0.f);
-                }
-            }
-        }
-        // read back: chunk q of the tile is row q / NCH, chunk q % NCH
-#pragma unroll
-        for (int s = 0; s < TM * NCH / 64; ++s) {
-            const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
-            const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (OC * 2) + ((ch ^ (row & (NCH - 1))) << 4));
-            const int grow = m0w + row;
-            if (grow < M) *reinterpret_cast<uint4*>(out + (int64_t)grow * ld_out + col0 + ch * 8) = v;
-        }
-    } else {
-        constexpr int NCH = TN / 4;  // 16-byte chunks (four fp32) per LDS row
-        // the two half-waves of a write are four rows apart; rows four apart start on the same
-        // bank, so every other group of four rows is shifted by eight chunks (128 bytes)
-        auto swz = [](int ch, int row) {
-            const int f = ((row >> 2) & 1) << 3;
-            return NCH % 16 == 0 ? (ch ^ f) : (ch + f) % NCH;
-        };
-        const int64_t col0 = (int64_t)tn * BN + wn * TN;
-        const int r_first = min(m0w, M - 1), r_last = min(m0w + TM - 1, M - 1);
-        const int b_first = r_first / L, b_last = r_last / L;
-        const int row_split = (b_first + 1) * L;
-        float g0[FN], g1[FN];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            g0[j] = gate[(int64_t)b_first * gate_stride + col0 + 32 * j + lc];
-            g1[j] = gate[(int64_t)b_last * gate_stride + col0 + 32 * j + lc];
-        }
-        // two passes of FM / 2 row tiles (64 rows x TN fp32)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-            for (int ii = 0; ii < FM / 2; ++ii) {
-                const int i = p * (FM / 2) + ii;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int c = 32 * j + lc;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int trow = 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-                        const int row = trow - p * (TM / 2);
-                        const float gv = m0w + trow < row_split ? g0[j] : g1[j];
-                        const float v = gv * (acc[i][j][r] * rsv[i][r] * cs[j]);
-                        const int off = row * (TN * 4) + (swz(c >> 2, row) << 4) + (c & 3) * 4;
-                        *reinterpret_cast<float*>(lds + off) = v;
-                    }
-                }
-            }
-            // read back four columns per lane, add the residual, store
-            constexpr int NS = (TM / 2) * NCH / 64;  // chunks per lane per pass
-            constexpr int SB = 8;                    // chunks per batch of residual loads
-            static_assert(NS % SB == 0, "batches");
-#pragma unroll
-            for (int s0 = 0; s0 < NS; s0 += SB) {
-                uint2 rv[SB];
-#pragma unroll
-                for (int s = 0; s < SB; ++s) {
-                    const int q = 64 * (s0 + s) + lane, row = q / NCH, ch = q % NCH;
-                    const int grow = min(m0w + p * (TM / 2) + row, M - 1);
-                    rv[s] = *reinterpret_cast<const uint2*>(resid + (int64_t)grow * N + col0 + ch * 4);
-                }
-#pragma unroll
-                for (int s = 0; s < SB; ++s) {
-                    const int q = 64 * (s0 + s) + lane, row = q / NCH, ch = q % NCH;
-                    const float4 v = *reinterpret_cast<const float4*>(lds + row * (TN * 4) + (swz(ch, row) << 4));
-                    const int grow = m0w + p * (TM / 2) + row;
-                    uint2 pk;
-                    pk.x = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].x) + v.x, bf16_to_f32((uint16_t)(rv[s].x >> 16)) + v.y);
-                    pk.y = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].y) + v.z, bf16_to_f32((uint16_t)(rv[s].y >> 16)) + v.w);
-                    if (grow < M) *reinterpret_cast<uint2*>(out + (int64_t)grow * N + col0 + ch * 4) = pk;
-                }
-            }
-        }
-    }
-}
-
-// Epilogue of a wave's TM x TN tile of 32x32 accumulators (TM = 32 FM,
 // TN = 32 FN) computed with the weight fragment as the MFMA's first operand,
 // so that acc[i][j] holds the transposed block: element r of acc[i][j] in lane
 // l is tile row 32 i + (l & 31) and B-tile column 32 j + 8 (r >> 2) + 4 (l >> 5)
@@ -178,7 +47,7 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 // (j, r >> 2): one row scale per i, the column scales four at a time, and one
 // 8-byte (bf16) or 16-byte (fp32) LDS write per four values.  The tile is
 // staged through the wave's own LDS region and read back in 16-byte row chunks
-// for the global stores, as in gemm_epilogue_lds.
+// for the global stores.
 //   STORE / SWIGLU: bf16 rows of OC = TN (TN / 2) columns, 16-byte chunk c of
 //     row r at physical chunk c ^ s(r) (s spreads the 32 rows of a write over
 //     the banks).
@@ -195,7 +64,7 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 // staging region (at least TM * TN * 2 bytes; the RESID padding needs
 // TM / 2 * (TN * 4 + 16)).
 template <int EPI, int BN, int TN, int FM, int FN>
-__device__ __forceinline__ void gemm_epilogue_lds_t(const v16f (&acc)[FM][FN], uint8_t* lds, int m0w, int wn, int tn,
+__device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uint8_t* lds, int m0w, int wn, int tn,
                                                     int lane, int M, int N, int L, uint16_t* out,
                                                     const uint16_t* resid, const float* rsl, const float* csl,
                                                     const float* gl, int bt0) {

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the ring is free once every wave is past its last read: each wave then stages its
     // epilogue in its own quarter of the LDS
     lds_barrier();
-    gemm_epilogue_lds_t<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
+    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
                                              resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
 }
 

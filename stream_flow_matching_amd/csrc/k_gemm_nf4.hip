@@ -20,7 +20,10 @@
 // spread over the substeps so that its VALU work runs beside the matrix cores.
 // One barrier per stage, before the last substep: it certifies that every wave
 // has read the stage (which frees its buffer for the stage two ahead) and that
-// the next stage's activation tile and decoded weights are complete.
+// the next stage's activation tile and decoded weights are complete.  The
+// weight fragment is the MFMA's first operand (transposed accumulator blocks:
+// a lane owns four consecutive output columns of a row), and the epilogue's
+// gate rows are loaded into LDS behind the ring at the start.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -98,6 +101,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int m0 = tm * BM;
     const int nks = K / kBK;
     if (tid < 16) lut[tid] = code.v[tid];
+    // the epilogue's factors go to LDS behind the ring: row and column scales (1: bf16 operands)
+    // and, for the gated residual, the gate rows of the (at most three) batches the tile's rows
+    // touch; written here, read after the main loop's barriers
+    float* scl = reinterpret_cast<float*>(smem + 2 * STAGE);
+    const int bt0 = EPI == SFM_EPI_RESID_GATE ? min(m0, M - 1) / L : 0;
+    for (int e = tid; e < BM + (EPI == SFM_EPI_RESID_GATE ? 4 : 1) * BN; e += 256) {
+        float v = 1.0f;
+        if (e >= BM + BN) {
+            const int g = (e - BM - BN) / BN, c = (e - BM - BN) % BN;
+            v = gate[(int64_t)min(bt0 + g, (M - 1) / L) * gate_stride + (int64_t)tn * BN + c];
+        }
+        scl[e] = v;
+    }
 
     // activation tile: wave-load v covers tile rows 8 (wave + 4 v) + (lane >> 3), physical chunk
     // lane & 7 holding logical chunk (lane & 7) ^ ((row >> 1) & 7)
@@ -167,8 +183,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     auto mfma = [&](int set, int q) {
         const int i = q / FN, j = q % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[set][FN + i]),
-                                                            __builtin_bit_cast(bf16x8, fr[set][j]), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fr[set][j]),
+                                                            __builtin_bit_cast(bf16x8, fr[set][FN + i]), acc[i][j], 0, 0, 0);
     };
     // substep: FM x FN MFMAs on `set`, with spread over them: the fragment reads of (rstg, rks)
     // into rset (if RD), decode part dp of `dslot` into dstg (if DEC), wave-loads v0 .. v1 (if DM)
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wait_vm_lgkm0<0>();
     lds_barrier();
     gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
-                                           resid, gate, gate_stride, nullptr, nullptr);
+                                             resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
 }
 
 template <int BM, int BN, int EPI>
@@ -244,7 +260,7 @@ hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, cons
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 1024;
+    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 1024 + (size_t)(BM + 4 * BN) * 4;
     auto kern = gemm_nf4_kernel<BM, BN, EPI>;
     static bool attr_set = false;
     if (!attr_set) {
