@@ -2,6 +2,8 @@
 // mapping of a workgroup's weight-tile rows onto weight rows.
 #pragma once
 
+#include <type_traits>
+
 #include "sfm_internal.h"
 
 namespace sfm {
@@ -117,13 +119,14 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
                 }
             }
         }
-        // read back: chunk q of the tile is row q / NCH, chunk q % NCH
+        // read back: chunk q of the tile is row q / NCH, chunk q % NCH; 32-bit offsets from the
+        // wave's first output element
+        uint16_t* const obase = out + (int64_t)m0w * ld_out + col0;
 #pragma unroll
         for (int s = 0; s < TM * NCH / 64; ++s) {
             const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
             const uint4 v = *reinterpret_cast<const uint4*>(lds + row * (OC * 2) + (swz(ch, row) << 4));
-            const int grow = m0w + row;
-            if (grow < M) *reinterpret_cast<uint4*>(out + (int64_t)grow * ld_out + col0 + ch * 8) = v;
+            if (m0w + row < M) *reinterpret_cast<uint4*>(obase + row * (int)ld_out + ch * 8) = v;
         }
     } else {
         constexpr int NCH = TN / 4;                   // 16-byte chunks (four fp32) per row
@@ -137,6 +140,10 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
         const int r_first = min(m0w, M - 1), r_last = min(m0w + TM - 1, M - 1);
         const int b_first = r_first / L, b_last = r_last / L;
         const int row_split = (b_first + 1) * L;
+        // 32-bit offsets from the wave's first row (residual rows past M are read as row M - 1)
+        const uint16_t* const rbase = resid + (int64_t)m0w * N + col0;
+        uint16_t* const obase = out + (int64_t)m0w * N + col0;
+        const bool full = m0w + TM <= M;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             // residual chunks of this pass first: their latency overlaps the staging writes
@@ -145,7 +152,7 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
             for (int s = 0; s < NS; ++s) {
                 const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
                 const int grow = min(m0w + PR * p + row, M - 1);
-                rv[s] = *reinterpret_cast<const uint2*>(resid + (int64_t)grow * N + col0 + ch * 4);
+                rv[s] = *reinterpret_cast<const uint2*>(rbase + (grow - m0w) * N + ch * 4);
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
@@ -173,16 +180,24 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's own staging writes
+            auto read_back = [&](auto guarded) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int q = 64 * s + lane, row = q / NCH, ch = q % NCH;
-                const v4f v = *reinterpret_cast<const v4f*>(lds + row * PITCH + (swz(ch, row) << 4));
-                const int grow = m0w + PR * p + row;
-                uint2 pk;
-                pk.x = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].x) + v[0], bf16_to_f32((uint16_t)(rv[s].x >> 16)) + v[1]);
-                pk.y = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].y) + v[2], bf16_to_f32((uint16_t)(rv[s].y >> 16)) + v[3]);
-                if (grow < M) *reinterpret_cast<uint2*>(out + (int64_t)grow * N + col0 + ch * 4) = pk;
-            }
+                for (int s = 0; s < NS; ++s) {
+                    const int q = 64 * s + lane, row = PR * p + q / NCH, ch = q % NCH;
+                    const v4f v = *reinterpret_cast<const v4f*>(lds + (q / NCH) * PITCH + (swz(ch, q / NCH) << 4));
+                    uint2 pk;
+                    pk.x = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].x) + v[0],
+                                      bf16_to_f32((uint16_t)(rv[s].x >> 16)) + v[1]);
+                    pk.y = cvt_bf16x2(bf16_to_f32((uint16_t)rv[s].y) + v[2],
+                                      bf16_to_f32((uint16_t)(rv[s].y >> 16)) + v[3]);
+                    if (!decltype(guarded)::value || m0w + row < M)
+                        *reinterpret_cast<uint2*>(obase + row * N + ch * 4) = pk;
+                }
+            };
+            if (full)
+                read_back(std::false_type{});
+            else
+                read_back(std::true_type{});
         }
     }
 }
