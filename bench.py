@@ -197,7 +197,7 @@ def text_project_bench(sfm, synth, ctx, M=512, iters=10):
     raw = synth.text_raw(M, k, ("bench_tp",), device="cuda")
     w = sfm.qweight(sfm.SFM_W_FP8_E4M3, wq, ws)
     out = torch.empty(M, D, dtype=torch.bfloat16, device="cuda")
-    wsp = sfm.workspace(sfm.lib().sfm_text_project_workspace_bytes(M, k))
+    wsp = sfm.workspace(sfm.lib().sfm_text_project_workspace_bytes(ctx.handle, M, k))
     sec = time_gpu(lambda: sfm.sfm_text_project(ctx, raw, norm_w, w, out, wsp), iters)
     fl = 2.0 * M * k * D
     return {"workload": f"{M} tokens x {k} raw features -> {D}", "us": round(sec * 1e6, 1),

@@ -334,8 +334,9 @@ int sfm_cfg_step_varlen(const sfm_context* ctx, const sfm_model_weights* cond, c
 
 /* ---------------------------------------------------------------- text conditioning *//* ---------------------------------------------------------------- text conditioning */
 
-/* Workspace bytes of sfm_text_project for M tokens of k_raw features. */
-size_t sfm_text_project_workspace_bytes(int M, int k_raw);
+/* Workspace bytes of sfm_text_project for M tokens of k_raw features (with
+ * room for the fp32 partial sums of a split-K projection when M is small). */
+size_t sfm_text_project_workspace_bytes(const sfm_context* ctx, int M, int k_raw);
 
 /* Projected text conditioning from raw text-encoder features (SimpleTuner
  * Ideogram 4 quick start, "Text embed cache": the text encoder concatenates 13
@@ -347,7 +348,9 @@ size_t sfm_text_project_workspace_bytes(int M, int k_raw);
  * every FP8 projection.  raw fp32 [M][k] (row-major), norm_w bf16 [k],
  * proj FP8 [emb_dim][k] with per-channel scales, text_out bf16 [M][emb_dim].
  * k = proj->k must be a multiple of 256 in [256, 65536].  M rows are
- * independent (batch and tokens flattened).  Errors: SFM_E_INVALID_ARG (NULL
+ * independent (batch and tokens flattened).  With few rows (a prompt) the
+ * projection splits K over up to 8 workgroups per output tile and reduces the
+ * fp32 partial sums before the scales and the bf16 rounding.  Errors: SFM_E_INVALID_ARG (NULL
  * or non-FP8 weight), SFM_E_SHAPE, SFM_E_WORKSPACE, SFM_E_ALIGN, SFM_E_DEVICE. */
 int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
                      uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream);

@@ -33,6 +33,8 @@
 // rows of the gated residual) are loaded into LDS behind the ring at the start,
 // under the first stages' loads.  Tiles are numbered XCD by XCD and, in each
 // XCD's range, in 8-row groups (L2 reuse of both operands).
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace sfm {
@@ -47,6 +49,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBK = 128;  // k bytes per stage
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kGroupM = 8;
+// epilogue of a split-K part: the raw fp32 sums of its k range (no scales), reduced by
+// splitk_reduce_kernel
+constexpr int kEpiPartial = 3;
 
 // s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (expcnt not waited on)
 template <int VM>
@@ -77,7 +82,7 @@ template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, uint16_t* out, const uint16_t* resid, const float* __restrict__ gate,
-    int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn) {
+    int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn, int kps, float* __restrict__ part) {
     constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int AI = BM / 32, BI = BN / 32;  // 1 KiB wave-loads per stage per wave
@@ -96,7 +101,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
-    grouped_tile(xcd_tile_id(), ntm, ntn, kGroupM, tm, tn);
+    // split-K (kps > 0): workgroup id = split * tiles + tile; split s walks k blocks of 256
+    // [s kps, (s + 1) kps), else the whole K
+    int tile = xcd_tile_id(), kbeg = 0, klen = K;
+    const int split = kps > 0 ? tile / (ntm * ntn) : 0;
+    if (kps > 0) {
+        tile -= split * ntm * ntn;
+        kbeg = split * kps * 256;
+        klen = min(K - kbeg, kps * 256);
+    }
+    grouped_tile(tile, ntm, ntn, kGroupM, tm, tn);
     const int m0 = tm * BM;
 
     // wave-load v of this wave covers tile rows 8 (wave + 4 v) + (lane >> 3); the lane writes
@@ -194,12 +208,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         scv[k] = v;
     }
 
-    // K % 256 == 0 (checked by the caller): nks >= 2 and even
-    const int nks = K / kBK;
+    // K % 256 == 0 (checked by the caller) and klen a multiple of 256: nks >= 2 and even
+    const int nks = klen / kBK;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) vmem(v, smem, ra, rb, 0);
+    for (int v = 0; v < NV; ++v) vmem(v, smem, ra, rb, kbeg);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) vmem(v, smem + STAGE, ra, rb, kBK);
+    for (int v = 0; v < NV; ++v) vmem(v, smem + STAGE, ra, rb, kbeg + kBK);
     wait_vm_lgkm0<NV>();
 #pragma unroll
     for (int k = 0; k < NSL; ++k)
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool more = t + 2 < nks;
         const __amdgpu_buffer_rsrc_t rA = more ? ra : ra0;
         const __amdgpu_buffer_rsrc_t rB = more ? rb : rb0;
-        const int k2 = (t + 2) * kBK;
+        const int k2 = kbeg + (t + 2) * kBK;
         quarter(0, 0, true, 1, cur, 1, 0, 0, cur, rA, rB, k2);
         wait_vm_lgkm0<63>();
         lds_barrier();
@@ -235,14 +249,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the ring is free once every wave is past its last read: each wave then stages its
     // epilogue in its own quarter of the LDS
     lds_barrier();
-    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
-                                             resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
+    if constexpr (EPI == kEpiPartial) {
+        // lane: row 32 i + (l & 31) of the wave tile, columns 32 j + 8 q + 4 (l >> 5) .. + 3
+        const int lc = lane & 31, lg = lane >> 5;
+        float* pbase = part + (size_t)split * M * N + (int64_t)tn * BN + wn * TN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = m0 + wm * TM + 32 * i + lc;
+            if (row < M)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<v4f*>(pbase + (int64_t)row * N + 32 * j + 8 * q + 4 * lg) =
+                            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+    } else {
+        gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L,
+                                               out, resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN,
+                                               bt0);
+    }
+}
+
+// out[m][n] = bf16((sum over the S parts of part[s][m][n]) * sa[m] * sw[n]); eight outputs per thread
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            const float* __restrict__ sa,
+                                                            const float* __restrict__ sw, uint16_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int n8 = N / 8;
+    if (i >= (int64_t)M * n8) return;
+    const int64_t m = i / n8;
+    const int n = (int)(i % n8) * 8;
+    v4f a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+        const float* p = part + ((size_t)s * M + m) * N + n;
+        a += *reinterpret_cast<const v4f*>(p);
+        b += *reinterpret_cast<const v4f*>(p + 4);
+    }
+    const float r = sa ? sa[m] : 1.0f;
+    const v4f c0 = sw ? *reinterpret_cast<const v4f*>(sw + n) : v4f{1.f, 1.f, 1.f, 1.f};
+    const v4f c1 = sw ? *reinterpret_cast<const v4f*>(sw + n + 4) : v4f{1.f, 1.f, 1.f, 1.f};
+    uint4 o;
+    o.x = cvt_bf16x2(a[0] * r * c0[0], a[1] * r * c0[1]);
+    o.y = cvt_bf16x2(a[2] * r * c0[2], a[3] * r * c0[3]);
+    o.z = cvt_bf16x2(b[0] * r * c1[0], b[1] * r * c1[1]);
+    o.w = cvt_bf16x2(b[2] * r * c1[2], b[3] * r * c1[3]);
+    *reinterpret_cast<uint4*>(out + m * N + n) = o;
 }
 
 template <int BM, int BN, int EPI>
 hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
-                      hipStream_t st) {
+                      hipStream_t st, int splits = 1, int kps = 0, float* part = nullptr) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
     // two ring stages, then the epilogue's scales (row, column and three gate rows)
@@ -253,8 +311,8 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), shm, st, a, sa, w, sw, out, resid, gate, gate_stride, M, N, K,
-                       L, ntm, ntn);
+    hipLaunchKernelGGL(kern, dim3(ntm * ntn * splits), dim3(256), shm, st, a, sa, w, sw, out, resid, gate, gate_stride,
+                       M, N, K, L, ntm, ntn, kps, part);
     return hipGetLastError();
 }
 
@@ -292,6 +350,32 @@ hipError_t launch_epi(const uint8_t* a, const float* sa, const uint8_t* w, const
 }
 
 }  // namespace
+
+int splitk_parts(int M, int N, int K) {
+    const int tiles = ((M + 255) / 256) * (N % 256 == 0 ? N / 256 : N / 128);
+    const int kb = K / 256;
+    if (tiles >= 128 || kb < 8) return 1;
+    const int want = std::min(8, std::max(1, 256 / tiles));
+    const int kps = (kb + want - 1) / want;
+    return (kb + kps - 1) / kps;
+}
+
+hipError_t launch_gemm_fp8_splitk(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
+                                  int M, int N, int K, float* part, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    const int S = splitk_parts(M, N, K);
+    const int kb = K / 256, kps = (kb + S - 1) / S;
+    hipError_t e = N % 256 == 0
+                       ? launch_cfg<256, 256, kEpiPartial>(a, sa, w, sw, out, nullptr, nullptr, 0, M, N, K, M, st, S,
+                                                           kps, part)
+                       : launch_cfg<256, 128, kEpiPartial>(a, sa, w, sw, out, nullptr, nullptr, 0, M, N, K, M, st, S,
+                                                           kps, part);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)M * (N / 8);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, S, M, N, sa,
+                       sw, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,

@@ -117,47 +117,61 @@ __global__ __launch_bounds__(kRowThreads) void adaln_kernel(const uint16_t* __re
 // E4M3 quantisation: the input side of the text-conditioning projection
 // (SimpleTuner Ideogram 4 quick start, "Text embed cache": 13 x 4096 fp32
 // features per token go through the frozen llm_cond_norm before
-// llm_cond_proj).  One workgroup per row, three passes: the sum of squares from
-// global memory, h = bf16(x * rinv * w) into LDS (cols * 2 bytes) with its
-// absolute maximum, then the codes from LDS.  Thread t owns the 4-element
-// groups 4 (t + 256 j) in every pass, so the LDS row needs no barrier between
-// writing and reading back.  cols % 4 == 0.
-__global__ __launch_bounds__(kRowThreads) void rmsnorm_f32_quant_kernel(const float* __restrict__ x, int cols,
-                                                                        const uint16_t* __restrict__ w,
-                                                                        uint8_t* __restrict__ q,
-                                                                        float* __restrict__ s, float eps) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t hrow[];
-    __shared__ float red[kRowWaves];
+// llm_cond_proj).  One workgroup of 1024 threads per row; thread t holds the
+// 4-element groups 4 (t + 1024 c), c < MAXC, in registers, so the row is read
+// once: sum of squares, h = bf16(x * rinv * w) with its absolute maximum, then
+// the codes.  cols % 4 == 0, cols <= 4096 MAXC.
+constexpr int kLongThreads = 1024;
+
+template <int MAXC>
+__global__ __launch_bounds__(kLongThreads) void rmsnorm_f32_quant_kernel(const float* __restrict__ x, int cols,
+                                                                         const uint16_t* __restrict__ w,
+                                                                         uint8_t* __restrict__ q,
+                                                                         float* __restrict__ s, float eps) {
+    __shared__ float red[kLongThreads / 64];
     const int64_t m = blockIdx.x;
     const float* row = x + m * cols;
+    float v[MAXC][4];
     float ss = 0.f;
-    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int i = 4 * (threadIdx.x + kLongThreads * c);
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < cols) u = *reinterpret_cast<const float4*>(row + i);
+        v[c][0] = u.x;
+        v[c][1] = u.y;
+        v[c][2] = u.z;
+        v[c][3] = u.w;
+        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
     }
-    ss = block_sum<kRowWaves>(ss, red);
+    ss = block_sum<kLongThreads / 64>(ss, red);
     const float rinv = 1.0f / sqrtf(ss / (float)cols + eps);
     float amax = 0.f;
-    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        const uint2 g = *reinterpret_cast<const uint2*>(w + i);
-        const float h0 = round_bf16((v.x * rinv) * __uint_as_float(g.x << 16));
-        const float h1 = round_bf16((v.y * rinv) * __uint_as_float(g.x & 0xFFFF0000u));
-        const float h2 = round_bf16((v.z * rinv) * __uint_as_float(g.y << 16));
-        const float h3 = round_bf16((v.w * rinv) * __uint_as_float(g.y & 0xFFFF0000u));
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(h0), fabsf(h1)), fmaxf(fabsf(h2), fabsf(h3))));
-        *reinterpret_cast<uint2*>(hrow + i) = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int i = 4 * (threadIdx.x + kLongThreads * c);
+        if (i < cols) {
+            const uint2 g = *reinterpret_cast<const uint2*>(w + i);
+            const float gw[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xFFFF0000u),
+                                 __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xFFFF0000u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[c][e] = round_bf16((v[c][e] * rinv) * gw[e]);
+                amax = fmaxf(amax, fabsf(v[c][e]));
+            }
+        }
     }
-    amax = block_max<kRowWaves>(amax, red);
+    amax = block_max<kLongThreads / 64>(amax, red);
     const float inv = amax > 0.f ? 448.0f / amax : 0.f;
-    for (int i = 4 * threadIdx.x; i < cols; i += 4 * kRowThreads) {
-        const uint2 h = *reinterpret_cast<const uint2*>(hrow + i);
-        uint32_t c = 0;
-        c = cvt_fp8x2<false>(clamp448(__uint_as_float(h.x << 16) * inv),
-                             clamp448(__uint_as_float(h.x & 0xFFFF0000u) * inv), c);
-        c = cvt_fp8x2<true>(clamp448(__uint_as_float(h.y << 16) * inv),
-                            clamp448(__uint_as_float(h.y & 0xFFFF0000u) * inv), c);
-        *reinterpret_cast<uint32_t*>(q + m * cols + i) = c;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int i = 4 * (threadIdx.x + kLongThreads * c);
+        if (i < cols) {
+            uint32_t code = 0;
+            code = cvt_fp8x2<false>(clamp448(v[c][0] * inv), clamp448(v[c][1] * inv), code);
+            code = cvt_fp8x2<true>(clamp448(v[c][2] * inv), clamp448(v[c][3] * inv), code);
+            *reinterpret_cast<uint32_t*>(q + m * cols + i) = code;
+        }
     }
     if (threadIdx.x == 0) s[m] = amax / 448.0f;
 }
@@ -310,15 +324,14 @@ hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, uint8_t* q, 
 hipError_t launch_rmsnorm_f32_quant(const float* x, int rows, int cols, const uint16_t* w, uint8_t* q, float* s,
                                     float eps, hipStream_t st) {
     if (rows == 0) return hipSuccess;
-    if (cols % 4 || cols > 65536) return hipErrorInvalidValue;
-    const size_t shm = (size_t)cols * 2;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)rmsnorm_f32_quant_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  65536 * 2);
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(rmsnorm_f32_quant_kernel, dim3(rows), dim3(kRowThreads), shm, st, x, cols, w, q, s, eps);
+    if (cols % 4) return hipErrorInvalidValue;
+    const int chunks = (cols / 4 + kLongThreads - 1) / kLongThreads;
+    if (chunks <= 4)
+        hipLaunchKernelGGL(rmsnorm_f32_quant_kernel<4>, dim3(rows), dim3(kLongThreads), 0, st, x, cols, w, q, s, eps);
+    else if (chunks <= 16)
+        hipLaunchKernelGGL(rmsnorm_f32_quant_kernel<16>, dim3(rows), dim3(kLongThreads), 0, st, x, cols, w, q, s, eps);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

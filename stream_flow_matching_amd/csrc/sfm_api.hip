@@ -647,11 +647,13 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
     return SFM_OK;
 }
 
-size_t sfm_text_project_workspace_bytes(int M, int k_raw) {
-    if (M < 0 || k_raw < 0) return 0;
+size_t sfm_text_project_workspace_bytes(const sfm_context* ctx, int M, int k_raw) {
+    if (!ctx || M < 0 || k_raw < 0) return 0;
     Carve c(nullptr);
     c.take<uint8_t>((size_t)M * k_raw);
     c.take<float>((size_t)M);
+    const int parts = splitk_parts(M, ctx->dims.emb_dim, k_raw);
+    if (parts > 1) c.take<float>((size_t)parts * M * ctx->dims.emb_dim);
     return c.off + 256;
 }
 
@@ -668,16 +670,24 @@ int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* n
     SFM_CHECK(check_ptr(text_out, "text_out"));
     SFM_CHECK(check_ptr(ws, "ws"));
     if (M < 0) return fail(SFM_E_SHAPE, "M < 0");
-    const size_t need = sfm_text_project_workspace_bytes(M, K);
+    const size_t need = sfm_text_project_workspace_bytes(ctx, M, K);
     if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     if (M == 0) return SFM_OK;
     Carve c(ws);
     uint8_t* codes = c.take<uint8_t>((size_t)M * K);
     float* scales = c.take<float>((size_t)M);
+    const int parts = splitk_parts(M, D, K);
+    float* part = parts > 1 ? c.take<float>((size_t)parts * M * D) : nullptr;
     const hipStream_t st = (hipStream_t)stream;
     SFM_LAUNCH(launch_rmsnorm_f32_quant(raw, M, K, norm_w, codes, scales, ctx->dims.eps, st));
-    SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, proj->scale, text_out, nullptr,
-                               nullptr, 0, M, D, K, M, st));
+    // a prompt has few rows and the features are long: split K when the output tiles alone would
+    // leave most of the compute units idle
+    if (parts > 1)
+        SFM_LAUNCH(launch_gemm_fp8_splitk(codes, scales, (const uint8_t*)proj->q, proj->scale, text_out, M, D, K, part,
+                                          st));
+    else
+        SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, proj->scale, text_out,
+                                   nullptr, nullptr, 0, M, D, K, M, st));
     return SFM_OK;
 }
 

@@ -165,6 +165,12 @@ hipError_t launch_timestep_embed(float t, float* e, int B, int dim, hipStream_t 
 hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
                            int K, int L, hipStream_t st);
+// Split-K FP8 STORE projection for few rows and long K (few output tiles): splitk_parts(M, N, K)
+// parts of fp32 partial sums in `part` ([parts][M][N]), then a reduce applying sa, sw and the
+// bf16 rounding.  1 part means the plain launch would fill the chip as well.
+int splitk_parts(int M, int N, int K);
+hipError_t launch_gemm_fp8_splitk(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
+                                  int M, int N, int K, float* part, hipStream_t st);
 
 // k_gemm_nf4.hip
 hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,

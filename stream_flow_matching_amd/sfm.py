@@ -114,7 +114,7 @@ SIGNATURES = {
                                  _P, _P, _F, _F, _F, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "sfm_sample_varlen": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P,
                                _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
-    "sfm_text_project_workspace_bytes": (_SZ, [_I, _I]),
+    "sfm_text_project_workspace_bytes": (_SZ, [_P, _I, _I]),
     "sfm_text_project": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _I, _P, _SZ, _P]),
     "sfm_time_grid": (_I, [_I, ctypes.c_double, ctypes.c_double, _I64, _P]),
     "sfm_preset": (_I, [_I, ctypes.POINTER(sfm_preset_info)]),
@@ -352,7 +352,7 @@ def sfm_text_project(ctx, raw, norm_w, proj, text_out, ws=None, stream=None):
     """raw fp32 [..., k] -> text_out bf16 [..., emb_dim]; proj a qweight (FP8)."""
     M = raw.numel() // raw.shape[-1]
     if ws is None:
-        ws = workspace(lib().sfm_text_project_workspace_bytes(M, raw.shape[-1]), raw.device)
+        ws = workspace(lib().sfm_text_project_workspace_bytes(ctx.handle, M, raw.shape[-1]), raw.device)
     _check(lib().sfm_text_project(ctx.handle, _ptr(raw), _ptr(norm_w), ctypes.byref(proj), _ptr(text_out), M,
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 

@@ -268,7 +268,7 @@ def test_linear_fp8_gated_residual_three_batches_per_tile(sfm, ctx_full, M, Nw, 
 
 # --------------------------------------------------------------------------- text conditioning projection
 
-@pytest.mark.parametrize("M,k", [(37, 1024), (1, 256), (300, 2048)])
+@pytest.mark.parametrize("M,k", [(37, 1024), (1, 256), (300, 2048), (37, 4352)])
 def test_text_project_tiny_width(sfm, ctx_tiny, M, k):
     """RMSNorm with weight + per-token E4M3 + FP8 projection to the tiny model
     width, all rows (ragged M) against the oracle."""
