@@ -348,6 +348,20 @@ def sfm_cfg_step_varlen(ctx, cond, uncond, text, text_lens, z, z_out, t, dt, gui
                                      _stream(stream)))
 
 
+def sfm_sample_varlen(ctx, cond: ModelWeights, uncond: ModelWeights, text, text_lens, z, z_out, t, guidance, B, T,
+                      gh, gw, ws, stream=None):
+    """sfm_sample for prompts of different text lengths (text padded to T rows)."""
+    import numpy as np
+    keep, p = _lens(text_lens)
+    t = np.ascontiguousarray(t, np.float64)
+    g = np.ascontiguousarray(guidance, np.float32)
+    if len(t) != len(g) + 1:
+        raise ValueError("t needs one more value than guidance")
+    _check(lib().sfm_sample_varlen(ctx.handle, ctypes.byref(cond.c), ctypes.byref(uncond.c), _ptr(text), p, _ptr(z),
+                                   _ptr(z_out), t.ctypes.data_as(_P), g.ctypes.data_as(_P), len(g), B, T, gh, gw,
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def sfm_text_project(ctx, raw, norm_w, proj, text_out, ws=None, stream=None):
     """raw fp32 [..., k] -> text_out bf16 [..., emb_dim]; proj a qweight (FP8)."""
     M = raw.numel() // raw.shape[-1]

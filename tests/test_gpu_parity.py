@@ -743,6 +743,32 @@ def test_sample_tiny_against_oracle_sampler(sfm, ctx_tiny):
     assert rel_l2(zo.cpu().numpy() - np64(z), ref - np64(z)) < 3e-2
 
 
+def test_sample_varlen_tiny(sfm, ctx_tiny):
+    """Two prompts of 16 and 6 text tokens through three guided steps: each
+    sample's latent change against the oracle sampler run on that sample alone
+    with its own text."""
+    from oracle import sampler as OS
+    _say("sample varlen tiny")
+    w = synth.Workload("tiny_svl2", synth.TINY, 2, 16, 16, 16, layers=2)
+    lens = [16, 6]
+    cond = synth.model_params(w.shape, 2, (0, "tiny_svc"))
+    unc = synth.model_params(w.shape, 2, (0, "tiny_svu"))
+    text, z, _, _ = synth.step_inputs(w)
+    cm, um = sfm.ModelWeights(to_device(cond)), sfm.ModelWeights(to_device(unc))
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 2, w.T, w.gh, w.gw))
+    t = sfm.sfm_time_grid(3, 0.0, 1.75, 256 * 256)
+    g = np.array([7.0, 7.0, 3.0], np.float32)
+    zo = torch.empty_like(z, device=DEV)
+    sfm.sfm_sample_varlen(ctx_tiny, cm, um, text.to(DEV), lens, z.to(DEV), zo, t, g, 2, w.T, w.gh, w.gw, ws)
+    torch.cuda.synchronize()
+    oc, ou = oracle_model(cond), oracle_model(unc)
+    for b, tb in enumerate(lens):
+        ref = OS.sample(np64(text[b:b + 1, :tb]) if tb else None, np64(z[b:b + 1]), list(t), list(g.astype(float)),
+                        oc, ou, w.gh, w.gw, O.TINY)
+        got = zo[b:b + 1].cpu().numpy()
+        assert rel_l2(got - np64(z[b:b + 1]), ref - np64(z[b:b + 1])) < 3e-2
+
+
 def _pinned(obj):
     """Copy of a synth dataclass with every tensor in pinned host memory."""
     import dataclasses
