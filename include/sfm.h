@@ -208,7 +208,13 @@ int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t
  * mask (research note: one shared self-attention over text + image tokens).
  * q, k bf16 [B][H][Lp][256], vt fp16 [B][H][256][Lp] as made by
  * sfm_qk_norm_rope; o bf16 [B*L][D], head h at columns h*256.. .  Scores in
- * fp32 from bf16 q k^T; the P V product in fp16 with fp32 accumulation. */
+ * fp32 from bf16 q k^T; the P V product in fp16 with fp32 accumulation.
+ * The (batch, head, 128-query block, 64-key tile) units are split evenly over
+ * one workgroup per compute unit; a query block shared by two workgroups is
+ * finished by a second kernel from fp32 partial results that this call keeps
+ * in a buffer owned by the context, so sfm_attention / sfm_attention_varlen
+ * calls on one context must not overlap in time (the block, model and step
+ * calls keep theirs in the caller's workspace instead). */
 int sfm_attention(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o,
                   int B, int L, void* stream);
 
@@ -300,7 +306,7 @@ int sfm_model_velocity_streamed(const sfm_context* ctx, const sfm_model_weights*
                                 const float* latent, float t, float* v_out, int B, int T, int gh, int gw, void* ws,
                                 size_t ws_bytes, void* stream);
 
-/* ---------------------------------------------------------------- variable text lengths *//* ---------------------------------------------------------------- variable text lengths */
+/* ---------------------------------------------------------------- variable text lengths */
 
 /* Batches of prompts with different text lengths.  The text prefixes are
  * padded to T rows in memory ([B][T + gh*gw][D] as everywhere); text_lens is

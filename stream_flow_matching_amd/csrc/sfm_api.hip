@@ -137,6 +137,7 @@ struct BlockWs {
     uint16_t* o;
     uint8_t* oq;  // also sq
     float* os;    // also ss
+    float* part;  // attention partial results
     size_t bytes;
 };
 
@@ -162,6 +163,7 @@ BlockWs plan_block(const sfm_dims* d, int B, int T, int gh, int gw, int wfmt, vo
         w.oq = c.take<uint8_t>(std::max(M * D, M * F));
         w.os = c.take<float>(M);
     }
+    w.part = c.take<float>(attention_part_bytes() / sizeof(float));
     w.bytes = c.off + 256;
     return w;
 }
@@ -218,10 +220,12 @@ struct LaunchTimer {
     int used;
 };
 
-// Enqueue one block; arguments already checked.
+// Enqueue one block; arguments already checked.  shared: another pass runs on the GPU at the
+// same time (the guided step), so attention takes one workgroup per query block, which the
+// hardware interleaves with the other pass's work, instead of the balanced persistent grid.
 int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
               const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
-              LaunchTimer* timer = nullptr) {
+              LaunchTimer* timer = nullptr, bool shared = false) {
     const bool timed = timer && timer->used < timer->n;
     auto mark = [&](void* const* ev) -> hipError_t {
         return timed ? hipEventRecord((hipEvent_t)ev[timer->used], st) : hipSuccess;
@@ -240,7 +244,7 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
     }
     SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T, gh,
                                    gw, H, d->eps, lens, st));
-    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, st));
+    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
     if (fmt == SFM_W_FP8_E4M3) {
         SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
@@ -369,7 +373,7 @@ int make_lens(const int32_t* text_lens, int B, int T, TextLens* out) {
 
 int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_t* text, const float* latent, float t,
               float* v_out, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
-              LaunchTimer* timer = nullptr) {
+              LaunchTimer* timer = nullptr, bool shared = false) {
     const sfm_dims* d = &ctx->dims;
     const int N = gh * gw, L = T + N, D = d->emb_dim, A = d->adaln_dim, C = d->latent_ch;
     StepWs w = plan_model(d, B, T, gh, gw, ws);
@@ -379,7 +383,8 @@ int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_
     if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
     SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
     for (int i = 0; i < mw->num_layers; ++i)
-        SFM_CHECK(run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, lens, timer));
+        SFM_CHECK(
+            run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, lens, timer, shared));
     SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
     SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
     SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
@@ -533,7 +538,9 @@ int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out) {
             sn[(size_t)p * 64 + j] = (float)sin(a);
         }
     build_nf4_codebook(ctx->nf4_code);
+    ctx->attn_grid = std::min(std::max(prop.multiProcessorCount, 1), kAttnMaxGrid);
     hipError_t e = hipMalloc((void**)&ctx->rope_cos, cs.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&ctx->attn_part, attention_part_bytes());
     if (e == hipSuccess) e = hipMalloc((void**)&ctx->rope_sin, sn.size() * sizeof(float));
     if (e == hipSuccess) e = hipMemcpy(ctx->rope_cos, cs.data(), cs.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(ctx->rope_sin, sn.data(), sn.size() * sizeof(float), hipMemcpyHostToDevice);
@@ -559,6 +566,7 @@ void sfm_context_destroy(sfm_context* ctx) {
     if (!ctx) return;
     if (ctx->rope_cos) (void)hipFree(ctx->rope_cos);
     if (ctx->rope_sin) (void)hipFree(ctx->rope_sin);
+    if (ctx->attn_part) (void)hipFree(ctx->attn_part);
     for (int i = 0; i < 2; ++i) {
         if (ctx->side[i]) (void)hipStreamDestroy(ctx->side[i]);
         if (ctx->join[i]) (void)hipEventDestroy(ctx->join[i]);
@@ -726,7 +734,8 @@ int sfm_attention(const sfm_context* ctx, const uint16_t* q, const uint16_t* k, 
     SFM_CHECK(check_ptr(vt, "vt"));
     SFM_CHECK(check_ptr(o, "o"));
     if (B < 1 || L < 1 || L > ctx->dims.max_text + 128 * 128) return fail(SFM_E_SHAPE, "B / L out of range");
-    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, 0, nullptr, (hipStream_t)stream));
+    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, 0, nullptr, ctx->attn_part, ctx->attn_grid,
+                                (hipStream_t)stream));
     return SFM_OK;
 }
 
@@ -741,7 +750,8 @@ int sfm_attention_varlen(const sfm_context* ctx, const uint16_t* q, const uint16
     if (T < 0 || T >= L) return fail(SFM_E_SHAPE, "text prefix T = %d must leave image keys (L = %d)", T, L);
     TextLens lens;
     SFM_CHECK(make_lens(text_lens, B, T, &lens));
-    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, T, &lens, (hipStream_t)stream));
+    SFM_LAUNCH(launch_attention(q, k, vt, o, B, L, ctx->dims.num_heads, T, &lens, ctx->attn_part, ctx->attn_grid,
+                                (hipStream_t)stream));
     return SFM_OK;
 }
 
@@ -919,8 +929,8 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
     const hipStream_t st = (hipStream_t)stream;
     if (timer) {
         // one pass after the other on the caller's stream, so that each timed launch runs alone
-        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, lp, timer));
-        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, nullptr, timer));
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, lp, timer, true));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, nullptr, timer, true));
     } else {
         // the passes are independent: each on its own stream, so that the last, partly filled
         // round of workgroups of one pass's kernels shares the GPU with the other pass
@@ -928,8 +938,8 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
         std::lock_guard<std::mutex> guard(cx->step_lock);
         SFM_TRY_HIP(hipEventRecord(cx->fork, st));
         for (int i = 0; i < 2; ++i) SFM_TRY_HIP(hipStreamWaitEvent(cx->side[i], cx->fork, 0));
-        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, cx->side[0], lp));
-        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, cx->side[1]));
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, cx->side[0], lp, nullptr, true));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, cx->side[1], nullptr, nullptr, true));
         for (int i = 0; i < 2; ++i) {
             SFM_TRY_HIP(hipEventRecord(cx->join[i], cx->side[i]));
             SFM_TRY_HIP(hipStreamWaitEvent(st, cx->join[i], 0));

@@ -16,6 +16,8 @@ struct sfm_context {
     float* rope_cos;      // device [max_pos][64] fp32
     float* rope_sin;      // device [max_pos][64] fp32
     float nf4_code[16];   // NF4 codebook (fp32), passed to kernels by value
+    int attn_grid = 0;    // attention workgroups: the device's compute units, at most 256
+    float* attn_part = nullptr;  // partial results of the standalone attention calls
     // the two passes of a CFG step run on these streams at once (default priority);
     // the fork / join events order them against the caller's stream, and the lock
     // keeps concurrent steps on one context from interleaving their use of them
@@ -184,9 +186,15 @@ hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const ui
                                int gw, int H, float eps, const TextLens* lens, hipStream_t st);
 
 // k_attn.hip
+// Attention runs as `grid` persistent workgroups (at most kAttnMaxGrid; one per compute unit)
+// that split the work evenly; items shared between workgroups leave partial results in `part`
+// (attention_part_bytes() bytes, private to the launch's stream until the launch completes).
+// grid 0: one workgroup per (batch, head, query block), no partial results.
+constexpr int kAttnMaxGrid = 256;
+size_t attention_part_bytes();
 // lens: per-sample text lengths of the T-row text prefixes (keys [len[b], T) masked), or NULL for none
 hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, uint16_t* o, int B, int L,
-                            int H, int T, const TextLens* lens, hipStream_t st);
+                            int H, int T, const TextLens* lens, float* part, int grid, hipStream_t st);
 
 // k_misc.hip
 hipError_t launch_euler_cfg(const float* z, const float* vc, const float* vu, float* zo, float* vo, int64_t n,

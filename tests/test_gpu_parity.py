@@ -410,6 +410,32 @@ def test_attention(sfm, ctx_tiny, ctx_full, B, L, H):
         assert rel_l2(got, ref) < 5e-3
 
 
+@pytest.mark.parametrize("B,L", [(1, 4608), (2, 1000), (3, 64)])
+def test_attention_pieces(sfm, ctx_tiny, B, L):
+    """Two heads over long sequences: one workgroup's share of the key tiles
+    is a fraction of a query block's walk, so most query blocks are split into
+    several pieces and finished by the merge kernel; every fifth row of every
+    sample against the oracle."""
+    _say("attention pieces", B, L)
+    H = 2
+    Lp = sfm.sfm_padded_len(L)
+    q = torch.zeros(B, H, Lp, 256, dtype=torch.bfloat16)
+    k = torch.zeros(B, H, Lp, 256, dtype=torch.bfloat16)
+    vt = torch.zeros(B, H, 256, Lp, dtype=torch.float16)
+    q[:, :, :L] = synth.bf16_normal((B, H, L, 256), ("apq", B, L), 1.0)
+    k[:, :, :L] = synth.bf16_normal((B, H, L, 256), ("apk", B, L), 1.0)
+    vt[:, :, :, :L] = synth.bf16_normal((B, H, 256, L), ("apv", B, L), 1.0).to(torch.float16)
+    o = torch.empty(B * L, H * 256, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_attention(ctx_tiny, q.to(DEV), k.to(DEV), vt[..., vt_order(Lp)].contiguous().to(DEV), o, B, L)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(np64(o)))
+    rows = np.r_[np.arange(0, L, 5), L - 1]
+    for b in range(B):
+        ref = N.bf16_round(O.attention(np64(q[b, :, :L]).transpose(1, 0, 2), np64(k[b, :, :L]).transpose(1, 0, 2),
+                                       np64(vt[b, :, :, :L]).transpose(2, 0, 1), rows=rows)).reshape(len(rows), -1)
+        assert rel_l2(np64(o[b * L + rows]), ref) < 5e-3
+
+
 def test_attention_large_scores(sfm, ctx_tiny):
     """Scores far above 2**8 in the exp2 domain exercise the running-max rescale."""
     _say("attention large")
@@ -594,8 +620,10 @@ def test_block_varlen_tiny(sfm, ctx_tiny):
 
 def test_block_varlen_full_sampled(sfm, ctx_full):
     """1024^2 block with two prompts (512 and 77 text tokens, padded to 512):
-    sampled rows of the short prompt against that prompt computed alone, and
-    the full-length prompt against the uniform call."""
+    sampled rows of each prompt against that prompt computed alone by the
+    oracle, and the full-length prompt against the uniform call.  (Attention
+    splits its key tiles over the workgroups by the batch's total work, so the
+    full-length prompt's rows match the uniform call to rounding, not bitwise.)"""
     _say("block varlen full")
     w = synth.Workload("full_vl", synth.FULL, 2, 512, 64, 64)
     lens = [512, 77]
@@ -609,10 +637,16 @@ def test_block_varlen_full_sampled(sfm, ctx_full):
     sfm.sfm_block_forward_varlen(ctx_full, bw, xd, xo, cd, 2, w.T, lens, w.gh, w.gw, ws)
     sfm.sfm_block_forward(ctx_full, bw, xd, xu, cd, 2, w.T, w.gh, w.gw, ws)
     torch.cuda.synchronize()
-    assert torch.equal(xo[0], xu[0])          # a full-length prompt is unaffected
+    sub = np.array([0, 40, 76, 77, 78, 511, 512, 1000, 2047, 4172, w.L - 1])
+    ref0 = O.block_forward(np64(x[0])[None], c[0:1].numpy().astype(np.float64), oracle_block(p), 512, w.gh, w.gw,
+                           O.IDEOGRAM4, rows=sub)
+    xin0 = np64(x[0])[sub]
+    for got0 in (np64(xo[0])[sub], np64(xu[0])[sub]):
+        assert rel_l2(got0, ref0) < 1e-2
+        assert rel_l2(got0 - xin0, ref0 - xin0) < UPDATE_BAR["fp8"]
     valid = np.r_[0:77, 512:w.L]
     xs = np64(x[1])[valid][None]
-    sub = np.array([0, 40, 76, 77, 78, 1000, 2047, 4172])
+    sub = np.array([0, 20, 40, 60, 76, 77, 78, 100, 300, 700, 1000, 1500, 2047, 2500, 3000, 3500, 4000, 4172])
     ref = O.block_forward(xs, c[1:2].numpy().astype(np.float64), oracle_block(p), 77, w.gh, w.gw, O.IDEOGRAM4,
                           rows=sub)
     got = np64(xo[1])[valid[sub]]
