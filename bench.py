@@ -188,6 +188,28 @@ def block_varlen_bench(sfm, synth, ctx, lens=(512, 77), iters=5):
             "ms": round(sec * 1e3, 4), "tokens_per_s": round(real / sec, 1), "tflops": round(fl / sec / 1e12, 2)}
 
 
+def attention_bench(sfm, ctx, L, iters=20):
+    """sfm_attention alone at one 1024^2 pass's shape (18 heads of 256, batch 1),
+    unit-RMS bf16 q and k and N(0,1) V: the balanced persistent grid plus its
+    merge of split query blocks.  4 L^2 256 H FLOP against the bf16 peak."""
+    import torch
+    H, d = 18, 256
+    Lp = sfm.sfm_padded_len(L)
+    g = torch.Generator(device="cuda").manual_seed(L)
+    q = torch.zeros(1, H, Lp, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    vt = torch.zeros(1, H, d, Lp, dtype=torch.float16, device="cuda")
+    q[:, :, :L] = torch.randn(1, H, L, d, generator=g, device="cuda").to(torch.bfloat16)
+    k[:, :, :L] = torch.randn(1, H, L, d, generator=g, device="cuda").to(torch.bfloat16)
+    vt[:, :, :, :L] = torch.randn(1, H, d, L, generator=g, device="cuda").to(torch.float16)
+    o = torch.empty(L, H * d, dtype=torch.bfloat16, device="cuda")
+    sec = time_gpu(lambda: sfm.sfm_attention(ctx, q, k, vt, o, 1, L), iters)
+    fl = 4.0 * L * L * d * H
+    return {"workload": f"attention alone, L {L}, 18 heads of 256 (balanced persistent grid + merge)",
+            "us": round(sec * 1e6, 1), "tflops": round(fl / sec / 1e12, 2),
+            "frac_bf16_peak": round(fl / sec / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def text_project_bench(sfm, synth, ctx, M=512, iters=10):
     """The text-conditioning projection of one 512-token prompt: 53,248 raw
     features per token to 4608 (RMSNorm + E4M3 + FP8 GEMM, K 53,248)."""
@@ -450,6 +472,8 @@ def main():
             extra[name] = block_bench(sfm, synth, ctx, name)
         extra["text_projection_512"] = text_project_bench(sfm, synth, ctx)
         extra["block_1024_varlen_b2"] = block_varlen_bench(sfm, synth, ctx)
+        extra["attention_4608"] = attention_bench(sfm, ctx, 4608)
+        extra["attention_4096"] = attention_bench(sfm, ctx, 4096)
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_sample)
 
     line = {

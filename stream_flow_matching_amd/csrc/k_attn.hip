@@ -126,8 +126,8 @@ struct UnitPos {
     int b, it;
     int64_t first;
 };
-__device__ __forceinline__ UnitPos locate_tail(int64_t u, int I0, int Hn, int L, int T, const TextLens& lens,
-                                               int varlen) {
+__host__ __device__ __forceinline__ UnitPos locate_tail(int64_t u, int I0, int Hn, int L, int T,
+                                                        const TextLens& lens, int varlen) {
     int b = I0 / Hn, i0 = I0 - b * Hn;
     int64_t pre = 0;
     for (;;) {
@@ -362,6 +362,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // compute of tile t; one barrier per tile.
         const int n = e1 - e0;
         ld.issue(st0, kw.key(e0));
+        // the q fragments must have arrived here, before the barrier (otherwise the compiler moves
+        // their loads behind it and the two latencies add up)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(qf[0][ks]));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int t = 0; t < n; t += 2) {
@@ -413,23 +417,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// Tail items split between neighbouring ranges: blocks (j, .) of the grid look at the boundary
-// u_j = j Ut / G and, when it lies inside an item and is that item's first inner boundary,
-// combines the item's pieces: the end piece of range j - 1 (slot 2 (j - 1) + 1) and the start
+// Tail items split between neighbouring ranges: the boundary u_j = j Ut / G that lies inside an
+// item and is that item's first inner boundary combines the item's pieces: the end piece of range j - 1 (slot 2 (j - 1) + 1) and the start
 // pieces of the non-empty ranges j, j + 1, ... that begin inside the item (slots 2 j', in order).
 // O = sum_s O_s 2^(m_s - m), l = sum_s l_s 2^(m_s - m), m = max_s m_s; o = O / l (each piece
 // stores O_s / l_s).
-// One 64-thread block per (boundary, wave slice of 16 queries): blockIdx.y is the slice.
+// The boundaries j that merge an item: u_j lies inside the item and is its first inner boundary.
+struct MergeList {
+    uint16_t j[kAttnMaxGrid];
+};
+__host__ __device__ inline bool merges_at(int j, int G, int R, int64_t Ut, int Hn, int L, int T, const TextLens& lens,
+                                          int varlen) {
+    if (j < 1) return false;
+    const int64_t uj = Ut * j / G;
+    if (uj >= Ut) return false;
+    const UnitPos pos = locate_tail(uj, R * G, Hn, L, T, lens, varlen);
+    return uj != pos.first && Ut * (j - 1) / G <= pos.first;
+}
+
+// One 64-thread block per (merging boundary, wave slice of 16 queries): blockIdx.x indexes the
+// list of merging boundaries, blockIdx.y is the slice.
 __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part, uint16_t* __restrict__ o,
                                                         int L, int H, int nqb, int T, TextLens lens, int varlen,
-                                                        int R, int64_t Ut) {
-    const int j = blockIdx.x, G = gridDim.x;
-    if (j == 0) return;
+                                                        int R, int64_t Ut, int G, MergeList ml) {
+    const int j = ml.j[blockIdx.x];
     const int64_t uj = Ut * j / G;
-    if (uj >= Ut) return;
     const UnitPos pos = locate_tail(uj, R * G, H * nqb, L, T, lens, varlen);
-    if (uj == pos.first) return;                       // the boundary falls between items
-    if (Ut * (j - 1) / G > pos.first) return;         // an earlier boundary inside this item merges it
     const int64_t item_end = pos.first + KeyWalk(L, T, varlen ? lens.len[pos.b] : T).nkt;
 
     const int lane = threadIdx.x, wave = blockIdx.y;
@@ -522,9 +535,15 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     const int G = R > 0 ? grid : (int)std::min<int64_t>(grid, Ut);
     hipLaunchKernelGGL(attn_kernel, dim3(G), dim3(512), 0, st, q, k, vt, o, part, L, Lp, H, nqb, T, tl, lens ? 1 : 0,
                        R, Ut);
-    if (G > 1 && Ut > 0)
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(G, 8), dim3(64), 0, st, part, o, L, H, nqb, T, tl, lens ? 1 : 0, R,
-                           Ut);
+    if (G > 1 && Ut > 0) {
+        MergeList ml;
+        int nm = 0;
+        for (int j = 1; j < G; ++j)
+            if (merges_at(j, G, R, Ut, Hn, L, T, tl, lens ? 1 : 0)) ml.j[nm++] = (uint16_t)j;
+        if (nm > 0)
+            hipLaunchKernelGGL(attn_merge_kernel, dim3(nm, 8), dim3(64), 0, st, part, o, L, H, nqb, T, tl,
+                               lens ? 1 : 0, R, Ut, G, ml);
+    }
     return hipGetLastError();
 }
 
