@@ -16,7 +16,9 @@ FP8-E4M3 / NF4 weight codes).  Citations name the source page and its section:
              "Training method" (flow matching, Euler, asymmetric CFG).
   [Deploy]   "Ideogram 4.0 free local deployment" blog post (post.smzdm.com),
              section 1.3 (asymmetric CFG, scale 4.0), section 2 (FP8 E4M3
-             original weights) and section 2.1 (NF4, block size 64, QLoRA).
+             original weights), section 2.1 (NF4, block size 64, QLoRA) and
+             section 2.2 (mixed scheme: 4-bit float FFN weights with block
+             scales, attention projections in FP8; here in the OCP MXFP4 form).
   [Note]     also section "Infra" (sampling presets) for the sampler.
   [Tuner]    SimpleTuner Ideogram 4 quick-start, sections "Text embed cache"
              (4608-d projected text features) and "Validation" (separate
@@ -29,6 +31,13 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
   nf4_codebook           endpoints -1, 0, 1; levels are evenly spaced normal
                          quantiles (scipy's inverse CDF)
   nf4/fp8 dequant        brute force per element
+  e2m1 / e8m0 / mxfp4    (tests/test_oracle_mxfp4.py) E2M1 table structure (sign,
+                         bias-1 binades, top value 6); brute-force nearest encode
+                         with ties to even; E8M0 vs torch's float8_e8m0fnu; nibble
+                         order; exact round trip of representable blocks; error
+                         bound incl. saturation; mxfp4_linear equals fp8_linear on
+                         weights both formats hold exactly; per-block scales; the
+                         mixed block equals the FP8 block on such weights
   silu, timestep_embedding   closed forms
   rms_normalize, adaln_norm  invariants (unit RMS, scale invariance, scale -1 -> 0)
   quantize_rows_e4m3, fp8_linear  identity on representable rows, brute-force

@@ -28,7 +28,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .numerics import (E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode,
-                       fp8_dequant_f32, nf4_dequant_f32)
+                       fp8_dequant_f32, mxfp4_dequant_f32, nf4_dequant_f32)
 
 
 @dataclass(frozen=True)
@@ -256,9 +256,33 @@ class Nf4Weight:
     k: int
 
 
+@dataclass
+class Mxfp4Weight:
+    packed: np.ndarray  # uint8 [N, K/2], element 2i in the low nibble of byte i
+    scales: np.ndarray  # uint8 E8M0 exponents [N, K/32]
+    n: int
+    k: int
+
+
+def mxfp4_linear(a_bf16, packed, scales, n, k):
+    """y[m, n] = (sum_k dec(Aq[m, k]) * w[n, k]) * (alpha[m] / 448), w = e2m1 * 2**(e - 127).
+
+    [Deploy] section 2.2: in the mixed scheme the FFN linears hold 4-bit float
+    weights with block scales; here MXFP4 (E2M1, one E8M0 scale per 32 elements
+    of a row).  The activation is quantised per token to E4M3 exactly as for
+    the FP8 weights, so the product runs on FP8 x FP4 matrix units; the float64
+    sum of products is exact.  No per-channel scale, no bias.
+    """
+    codes, alpha = quantize_rows_e4m3(a_bf16)
+    acc = e4m3_decode(codes) @ mxfp4_dequant_f32(packed, scales, n, k).astype(np.float64).T
+    return acc * (alpha / E4M3_MAX)[:, None]
+
+
 def linear(a_bf16, w):
     if isinstance(w, Fp8Weight):
         return fp8_linear(a_bf16, w.codes, w.scale)
+    if isinstance(w, Mxfp4Weight):
+        return mxfp4_linear(a_bf16, w.packed, w.scales, w.n, w.k)
     return nf4_linear(a_bf16, w.packed, w.absmax, w.n, w.k)
 
 
@@ -266,6 +290,8 @@ def row_slice(w, r0, r1):
     """Output rows [r0, r1) of a quantised weight (for the q / k / v and gate / up parts)."""
     if isinstance(w, Fp8Weight):
         return Fp8Weight(w.codes[r0:r1], w.scale[r0:r1])
+    if isinstance(w, Mxfp4Weight):
+        return Mxfp4Weight(w.packed[r0:r1], np.asarray(w.scales).reshape(w.n, w.k // 32)[r0:r1], r1 - r0, w.k)
     blocks_per_row = w.k // 64
     return Nf4Weight(w.packed[r0:r1], np.asarray(w.absmax).reshape(w.n, blocks_per_row)[r0:r1].reshape(-1),
                      r1 - r0, w.k)

@@ -8,6 +8,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 * FP8 E4M3: the released weights are FP8 E4M3 ([Deploy] section 2).  The
   variant is the OCP E4M3FN one: exponent bias 7, no infinities, NaN only at
   S.1111.111, largest finite 448, subnormals m * 2**-9.
+* MXFP4: [Deploy] section 2.2 describes a mixed scheme with the FFN layers in
+  4-bit floats (torch.float4_e2m1fn elements, block scales) and the attention
+  projections kept in FP8.  The gfx950 form here is OCP MXFP4: E2M1 elements,
+  one E8M0 power-of-two scale per 32 consecutive elements of a row.
 * NF4: [Deploy] section 2.1 names QLoRA's NormalFloat-4 with block size 64.
   The codebook printed there (ending at 1.6368) cannot be an absmax-scaled
   code (its values exceed 1), so the codebook here is rebuilt from the QLoRA
@@ -160,6 +164,101 @@ def nf4_dequant_f32(packed, absmax, n: int, k: int) -> np.ndarray:
     am = np.asarray(absmax, dtype=np.float32).reshape(n, k // 64)
     am_full = np.repeat(am, 64, axis=1)
     return (code[q].astype(np.float32) * am_full).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- MXFP4
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (float64).
+
+    Code bits s.ee.m: sign s, exponent field e (bias 1), one mantissa bit m.
+    e = 0 is the subnormal binade, value m * 2**-1; e > 0 gives
+    (1 + m/2) * 2**(e - 1).  The largest finite magnitude is 6; there are no
+    infinities or NaNs.  ([Deploy] section 2.2 names torch.float4_e2m1fn as the
+    element type of the 4-bit layers.)
+    """
+    c = np.asarray(codes).astype(np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(s == 1, -mag, mag)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Nearest E2M1 code, ties to the even mantissa bit, |x| > 6 saturating to 6.
+
+    Implemented by rounding |x| on the uniform grid of its binade: the grid
+    step is 0.5 below 2, 1 in [2, 4) and 2 in [4, 8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 6.0)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    q = a / step
+    r = np.floor(q)
+    frac = q - r
+    up = (frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1))
+    v = (r + up) * step                       # may step into the next binade (exact)
+    v = np.minimum(v, 6.0)
+    # code from the value: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 are codes 0..7
+    mag_code = np.where(v < 2.0, np.round(v * 2.0), np.where(v < 4.0, v + 2.0, v / 2.0 + 4.0)).astype(np.int64)
+    sign = ((x < 0) & (mag_code > 0)).astype(np.int64)
+    return (sign << 3 | mag_code).astype(np.uint8)
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 block scale 2**(code - 127) (float64); code 255 is NaN."""
+    c = np.asarray(codes).astype(np.int64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def mxfp4_quantize(w, block=32):
+    """(codes uint8 [n, k], scale exponents uint8 [n, k/block]) of w [n, k].
+
+    OCP Microscaling, FP4 (E2M1) elements: each block of 32 consecutive
+    elements of a row shares the scale 2**X with X = floor(log2(amax)) - 2
+    (2 is the largest E2M1 exponent, so amax / 2**X lies in [4, 8) and values
+    above 6 saturate); elements are e2m1_encode(w / 2**X).  An all-zero block
+    gets exponent code 0.  This is the gfx950 analogue of the 4-bit FFN layers
+    of the mixed scheme in [Deploy] section 2.2 (NVIDIA's variant: E4M3 scales
+    over other block sizes).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    n, k = w.shape
+    if k % block:
+        raise ValueError("k must be a multiple of the block size")
+    wb = w.reshape(n, k // block, block)
+    amax = np.abs(wb).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2.0, -127.0)
+    X = np.clip(X, -127.0, 127.0)
+    codes = e2m1_encode(wb / np.exp2(X)[:, :, None]).reshape(n, k)
+    return codes, (X + 127.0).astype(np.uint8)
+
+
+def mxfp4_pack(codes) -> np.ndarray:
+    """Bytes [n, k/2] of codes [n, k]: element 2i in the low nibble of byte i, 2i+1 in the high
+    nibble (the order the gfx950 matrix cores read 4-bit operands)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def mxfp4_unpack(packed, n: int, k: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8).reshape(n, k // 2)
+    out = np.empty((n, k), dtype=np.uint8)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def mxfp4_dequant_f32(packed, scales, n: int, k: int) -> np.ndarray:
+    """fp32 weight w[n, k] = e2m1(q[n, k]) * 2**(e[n, k // 32] - 127); exact in fp32 (a 2-bit
+    significand times a power of two no smaller than 2**-128)."""
+    if k % 32:
+        raise ValueError("MXFP4 blocks of 32 need k % 32 == 0")
+    q = mxfp4_unpack(packed, n, k)
+    sc = np.repeat(e8m0_decode(np.asarray(scales, np.uint8).reshape(n, k // 32)), 32, axis=1)
+    return (e2m1_decode(q) * sc).astype(np.float32)
 
 
 def fp8_dequant_f32(codes, scale) -> np.ndarray:

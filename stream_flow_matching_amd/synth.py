@@ -19,6 +19,11 @@ quantisation section; NF4 block 64 per its NF4 subsection):
     near-equiprobable for normal weights), one element per 64-block forced to
     an extreme level (+-1, the absmax element), absmax = max |N(0, 0.02**2)|
     over 64 draws.
+  * MXFP4 (the 4-bit FFN layers of the mixed scheme, deployment post section
+    2.2): E2M1 codes uniform over the 16 levels, one element per 32-block
+    forced to +-6 (the block maximum), E8M0 exponents uniform in 119..121 (the
+    block scales N(0, 0.02**2) weights give).  The "mixed" block keeps QKV and
+    the output projection in FP8 and puts gate/up and down in MXFP4.
   * small layers (latent embed, timestep MLP, final layer): N(0, 1/fan_in) in
     bf16; modulation weights N(0, 0.02**2) bf16 with zero bias; QK-norm
     weights 1 + N(0, 0.02**2) in bf16.
@@ -93,6 +98,24 @@ def nf4_weight(n, k, key, std=0.02, device="cpu"):
     absmax = draws.abs().amax(dim=1).contiguous()
     packed = ((q[:, 0::2] << 4) | q[:, 1::2]).to(torch.uint8).contiguous()
     return packed, absmax
+
+
+def mxfp4_weight(n, k, key, device="cpu"):
+    """(packed uint8 [n, k/2], exponents uint8 [n, k/32]) per the MXFP4 recipe above.
+
+    Element 2i of a row is the low nibble of byte i, 2i+1 the high nibble.
+    """
+    if k % 32:
+        raise ValueError("k must be a multiple of 32 for MXFP4 blocks")
+    g = _gen(key + ("codes",), device)
+    q = torch.randint(0, 16, (n, k), generator=g, device=device, dtype=torch.int32)
+    nb = n * k // 32
+    where = torch.randint(0, 32, (nb,), generator=g, device=device)
+    ext = torch.where(torch.rand(nb, generator=g, device=device) < 0.5, 7, 15).to(torch.int32)
+    q.view(nb, 32).scatter_(1, where[:, None], ext[:, None])
+    e = torch.randint(119, 122, (n, k // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8).contiguous()
+    return packed, e.contiguous()
 
 
 # --------------------------------------------------------------------------- workloads
@@ -175,14 +198,16 @@ def text_raw(M, k, key, device="cpu"):
 
 
 def block_params(shape: Shape, key, fmt="fp8", device="cpu") -> BlockParams:
+    """fmt "fp8", "nf4", or "mixed" (QKV and output projection FP8, gate/up and down MXFP4)."""
     D, F = shape.emb_dim, shape.intermediate
-    mk = fp8_weight if fmt == "fp8" else nf4_weight
+    mk = fp8_weight if fmt in ("fp8", "mixed") else nf4_weight
+    mk_ffn = (lambda n, k, key, device: mxfp4_weight(n, k, key, device)) if fmt == "mixed" else mk
     return BlockParams(
         fmt=fmt,
         qkv=mk(3 * D, D, key + ("qkv",), device=device),
         o=mk(D, D, key + ("o",), device=device),
-        gate_up=mk(2 * F, D, key + ("gate_up",), device=device),
-        down=mk(D, F, key + ("down",), device=device),
+        gate_up=mk_ffn(2 * F, D, key + ("gate_up",), device=device),
+        down=mk_ffn(D, F, key + ("down",), device=device),
         q_norm=bf16_normal((256,), key + ("q_norm",), 0.02, 1.0, device),
         k_norm=bf16_normal((256,), key + ("k_norm",), 0.02, 1.0, device),
         mod_w=bf16_normal((4 * D, shape.adaln_dim), key + ("mod_w",), 0.02, device=device),

@@ -19,7 +19,10 @@ def npu8(t: torch.Tensor) -> np.ndarray:
 
 def oracle_weight(fmt, pair):
     q, s = pair
-    if fmt == "fp8":
+    if s.dtype == torch.uint8:                     # MXFP4: E8M0 exponents [n][k/32]
+        n, k2 = q.shape
+        return O.Mxfp4Weight(npu8(q), npu8(s), n, 2 * k2)
+    if fmt in ("fp8", "mixed"):
         return O.Fp8Weight(npu8(q), s.detach().cpu().numpy().astype(np.float32))
     n, k2 = q.shape
     return O.Nf4Weight(npu8(q), s.detach().cpu().numpy().astype(np.float32), n, 2 * k2)
