@@ -93,23 +93,31 @@ int sfm_positions(int T, int gh, int gw, int32_t* pos_host);
 
 typedef enum sfm_wfmt {
     SFM_W_FP8_E4M3 = 1, /* q: uint8 E4M3 codes [n][k]; scale: fp32 [n] per output channel */
-    SFM_W_NF4_B64 = 2   /* q: uint8 [n][k/2] nibbles (element 2i = high nibble of byte i);
+    SFM_W_NF4_B64 = 2,  /* q: uint8 [n][k/2] nibbles (element 2i = high nibble of byte i);
                            scale: fp32 absmax [n*k/64], one per 64 consecutive elements */
+    SFM_W_MXFP4 = 3     /* q: uint8 [n][k/2] E2M1 nibbles (element 2i = LOW nibble of byte i);
+                           scale: uint8 E8M0 exponents [n][k/32], one per 32 consecutive elements */
 } sfm_wfmt;
 
 /* A quantised weight W[n][k] (out x in).  FP8: w = decode(q) * scale[n]
  * (deployment post, section 2: original release FP8 E4M3).  NF4: w =
  * fp32(code[q] * absmax[block]) with the 16-level normal-quantile codebook
- * (deployment post, section 2.1: NF4, block size 64). */
+ * (deployment post, section 2.1: NF4, block size 64).  MXFP4: w = e2m1(q) *
+ * 2^(e - 127), the OCP microscaling form of the 4-bit float FFN weights of the
+ * deployment post's mixed scheme (section 2.2); its products run on FP8 x FP4
+ * matrix cores with the activation quantised per token to E4M3, as for FP8.
+ * `scale` points to fp32 values for FP8 and NF4 and to uint8 exponents for
+ * MXFP4. */
 typedef struct sfm_qweight {
     int32_t fmt, n, k;
     const void* q;
-    const float* scale;
+    const void* scale;
 } sfm_qweight;
 
 /* One block's weights.  qkv [3D][D] (rows: q heads, k heads, v heads, head h
  * at rows h*256..h*256+255 of each part); o [D][D]; gate_up [2F][D] (gate rows
- * [0, F), up rows [F, 2F)); down [D][F].  All four in one format.  q_norm,
+ * [0, F), up rows [F, 2F)); down [D][F].  All four in one format, or "mixed"
+ * (deployment post, section 2.2): qkv and o FP8, gate_up and down MXFP4.  q_norm,
  * k_norm: bf16 [256] QK-RMSNorm weights shared by the heads.  mod_w bf16
  * [4D][A], mod_b fp32 [4D]: AdaLN map from the timestep embedding to
  * (scale_attn, gate_attn, scale_mlp, gate_mlp). */
@@ -227,7 +235,8 @@ int sfm_euler_cfg(const float* z, const float* v_c, const float* v_u, float* z_o
 
 /* Dequantise a weight to out [n][k]: out_dtype 0 = fp32, 1 = bf16 (RNE of the
  * fp32 value).  FP8: fp32(decode(q) * scale[n]); NF4: fp32(code[q] *
- * absmax[block]).  Bit-exact by definition. */
+ * absmax[block]); MXFP4: e2m1(q) * 2^(e - 127) (exact in fp32 and bf16).
+ * Bit-exact by definition. */
 int sfm_dequant(const sfm_context* ctx, const sfm_qweight* w, void* out, int out_dtype, void* stream);
 
 /* --------------------------------------------------------- block / model / step */

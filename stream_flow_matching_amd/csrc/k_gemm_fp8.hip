@@ -78,23 +78,39 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SFM_LDS(lds), 16, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int EPI>
+// LDS of one configuration: the two-stage ring (also the epilogue's staging, a quarter per
+// wave), then the epilogue's scales.  WF 0: FP8 weights (128 bytes per row and stage); WF 1:
+// MXFP4 weights (64 bytes per row and stage).
+template <int BM, int BN, int EPI, int WF>
+struct GemmLds {
+    static constexpr int TM = BM / 2, TN = BN / 2;
+    static constexpr int WROW = WF ? kBK / 2 : kBK;
+    static constexpr int STAGE = BM * kBK + BN * WROW;
+    static constexpr int EPI_BYTES = EPI == SFM_EPI_RESID_GATE ? TM / 2 * (TN * 4 + ((TN / 4) % 16 ? 16 : 0))
+                                     : EPI == kEpiPartial      ? 0
+                                                               : TM * (EPI == SFM_EPI_SWIGLU ? TN / 2 : TN) * 2;
+    static constexpr int RING = 2 * STAGE > 4 * EPI_BYTES ? 2 * STAGE : 4 * EPI_BYTES;
+    static constexpr size_t BYTES = (size_t)RING + (size_t)(BM + 4 * BN) * 4;
+};
+
+template <int BM, int BN, int EPI, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, uint16_t* out, const uint16_t* resid, const float* __restrict__ gate,
-    int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn, int kps, float* __restrict__ part) {
+    const float* __restrict__ sw, const uint8_t* __restrict__ wexp, uint16_t* out, const uint16_t* resid,
+    const float* __restrict__ gate, int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn, int kps,
+    float* __restrict__ part) {
+    constexpr bool MX = WF == 1;
+    using Lds = GemmLds<BM, BN, EPI, WF>;
     constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
-    constexpr int AI = BM / 32, BI = BN / 32;  // 1 KiB wave-loads per stage per wave
+    // 1 KiB wave-loads per stage per wave: A 8 rows x 128 bytes each; W the same for FP8, 16
+    // rows x 64 bytes for MXFP4
+    constexpr int AI = BM / 32, BI = MX ? BN / 64 : BN / 32;
     constexpr int NV = AI + BI;                // vector-memory ops per stage per wave
     constexpr int NF = FM + FN;                // fragments per half-stage
     constexpr int NQ = (FM / 2) * FN;          // MFMAs per quarter-stage
-    constexpr int STAGE = (BM + BN) * kBK;
+    constexpr int STAGE = Lds::STAGE, WROW = Lds::WROW;
     static_assert(FM % 2 == 0, "quarter-stages split the row tiles in two");
-    // each wave stages its epilogue in a quarter of the ring
-    static_assert((EPI == SFM_EPI_RESID_GATE ? TM / 2 * (TN * 4 + ((TN / 4) % 16 ? 16 : 0))
-                                             : TM * (EPI == SFM_EPI_SWIGLU ? TN / 2 : TN) * 2) <= STAGE / 2,
-                  "epilogue staging fits the wave's quarter of the ring");
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -130,15 +146,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll
     for (int v = 0; v < BI; ++v) {
-        const int64_t wr = weight_row<EPI, BN, TN>(8 * (wave + 4 * v) + lrow, tn, N);
-        voff[AI + v] = (uint32_t)wr * (uint32_t)K + lch * 16;
+        if constexpr (MX) {
+            // 16 rows of 64 bytes: lane l row 16 (wave + 4 v) + (l >> 2), physical chunk l & 3 =
+            // logical chunk ^ ((row >> 2) & 3) = logical ^ ((l >> 4) & 3)
+            const int64_t wr = weight_row<EPI, BN, TN>(16 * (wave + 4 * v) + (lane >> 2), tn, N);
+            voff[AI + v] = (uint32_t)wr * (uint32_t)(K / 2) + (((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+        } else {
+            const int64_t wr = weight_row<EPI, BN, TN>(8 * (wave + 4 * v) + lrow, tn, N);
+            voff[AI + v] = (uint32_t)wr * (uint32_t)K + lch * 16;
+        }
     }
     // LDS destination of wave-load v inside a stage (uniform per wave)
     auto vmem = [&](int v, uint8_t* stg, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, int k0) {
         if (v < AI)
             dma16(rA, stg + wave * 1024 + v * 4096, voff[v], k0);
         else
-            dma16(rB, stg + BM * kBK + wave * 1024 + (v - AI) * 4096, voff[v], k0);
+            dma16(rB, stg + BM * kBK + wave * 1024 + (v - AI) * 4096, voff[v], MX ? k0 / 2 : k0);
     };
 
     v16f acc[FM][FN];
@@ -150,22 +173,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // fragment rows have (row >> 1) & 7 == (lr >> 1) & 7: chunk offsets are per-lane constants;
     // half h of a 128-byte row holds logical chunks 4h .. 4h + 3
     const int lr = lane & 31, lg = lane >> 5, sx = (lr >> 1) & 7;
-    const int cc[2][2] = {{((2 * lg) ^ sx) << 4, ((2 * lg + 1) ^ sx) << 4},
-                          {((4 + 2 * lg) ^ sx) << 4, ((4 + 2 * lg + 1) ^ sx) << 4}};
-    const int arow = (wm * TM + lr) * kBK, brow = BM * kBK + (wn * TN + lr) * kBK;
+    // MXFP4: the FP4 operand's lane (row, half g) holds 16 values at k 16 g + t and 16 at
+    // 32 + 16 g + t (t < 16), and its E8M0 scale covers all 32.  Numbering the k of each 64-k half
+    // so that a W lane holds the 32 consecutive k of one MX block, lane g of W reads logical
+    // chunk 2 h + g of its 64-byte row and the FP8 activation lane g reads chunks g and 2 + g of
+    // the half (instead of 2 g and 2 g + 1)
+    const int cc[2][2] = {{((MX ? lg : 2 * lg) ^ sx) << 4, ((MX ? 2 + lg : 2 * lg + 1) ^ sx) << 4},
+                          {((MX ? 4 + lg : 4 + 2 * lg) ^ sx) << 4, ((MX ? 6 + lg : 4 + 2 * lg + 1) ^ sx) << 4}};
+    const int cw[2] = {((0 + lg) ^ ((lr >> 2) & 3)) << 4, ((2 + lg) ^ ((lr >> 2) & 3)) << 4};
+    const int arow = (wm * TM + lr) * kBK, brow = BM * kBK + (wn * TN + lr) * WROW;
 
     // fragment f of a half: f < FN is weight column tile f, else row tile f - FN
     v8i fr[2][NF];
     auto ds = [&](int set, int f, const uint8_t* stg, int h) {
+        if (MX && f < FN) {
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(stg + brow + f * 32 * WROW + cw[h]);
+            fr[set][f] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, 0, 0, 0, 0};
+            return;
+        }
         const uint8_t* p = stg + (f < FN ? brow + f * 32 * kBK : arow + (f - FN) * 32 * kBK);
         const u32x4 x0 = *reinterpret_cast<const u32x4*>(p + cc[h][0]);
         const u32x4 x1 = *reinterpret_cast<const u32x4*>(p + cc[h][1]);
         fr[set][f] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
+    // MXFP4 block exponents of the stage: one 32-bit word (the stage's four blocks) per W fragment
+    // row; lane g of half h uses byte 2 h + g.  Loaded one stage ahead.
+    uint32_t eoff[FN], su[FN], sn[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        eoff[j] = MX ? (uint32_t)weight_row<EPI, BN, TN>(wn * TN + 32 * j + lr, tn, N) * (uint32_t)(K / 32) +
+                           (uint32_t)(kbeg / 32)
+                     : 0u;
+        su[j] = sn[j] = 0u;
+    }
+    auto load_exp = [&](uint32_t (&dst)[FN], int t) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) dst[j] = *reinterpret_cast<const uint32_t*>(wexp + eoff[j] + 4 * t);
+    };
     auto mfma = [&](int set, int q, int i0) {
         const int i = i0 + q / FN, j = q % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][j], fr[set][FN + i], acc[i][j], 0, 0, 0,
-                                                                    0, 0, 0);
+        if constexpr (MX)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][j], fr[set][FN + i], acc[i][j], 4, 0, 0,
+                                                                        (int)(su[j] >> (16 * set + 8 * lg)), 0, 127);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[set][j], fr[set][FN + i], acc[i][j], 0, 0, 0,
+                                                                        0, 0, 0);
     };
     // quarter-stage: NQ MFMAs on fragment set `set`, row tiles i0 .. i0 + FM/2, with the
     // fragment reads for set `rset` from half rh of rstg (if RD) and wave-loads v0 .. v1 into
@@ -189,7 +241,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // touch [3][BN]; their loads are issued before the first stages' and land under them
     constexpr int NSC = BM + (EPI == SFM_EPI_RESID_GATE ? 4 : 1) * BN;
     constexpr int NSL = (NSC + 255) / 256;
-    float* scl = reinterpret_cast<float*>(smem + 2 * STAGE);
+    float* scl = reinterpret_cast<float*>(smem + Lds::RING);
     const int bt0 = EPI == SFM_EPI_RESID_GATE ? min(m0, M - 1) / L : 0;
     float scv[NSL];
 #pragma unroll
@@ -210,6 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // K % 256 == 0 (checked by the caller) and klen a multiple of 256: nks >= 2 and even
     const int nks = klen / kBK;
+    if constexpr (MX) load_exp(su, 0);
 #pragma unroll
     for (int v = 0; v < NV; ++v) vmem(v, smem, ra, rb, kbeg);
 #pragma unroll
@@ -235,6 +288,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const __amdgpu_buffer_rsrc_t rA = more ? ra : ra0;
         const __amdgpu_buffer_rsrc_t rB = more ? rb : rb0;
         const int k2 = kbeg + (t + 2) * kBK;
+        // the next stage's block exponents go out before this stage's loads (the waits below
+        // then cover them)
+        if constexpr (MX)
+            if (t + 1 < nks) load_exp(sn, t + 1);
         quarter(0, 0, true, 1, cur, 1, 0, 0, cur, rA, rB, k2);
         wait_vm_lgkm0<63>();
         lds_barrier();
@@ -243,6 +300,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         wait_vm_lgkm0<V2>();
         lds_barrier();
         quarter(1, FM / 2, true, 0, nxt, 0, V2, NV, cur, rA, rB, k2);
+        if constexpr (MX)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) su[j] = sn[j];
     }
     wait_vm_lgkm0<0>();
 
@@ -265,7 +325,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                             v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
     } else {
-        gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L,
+        gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (Lds::RING / 4), m0 + wm * TM, wn, tn, lane, M, N, L,
                                                out, resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN,
                                                bt0);
     }
@@ -297,22 +357,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     *reinterpret_cast<uint4*>(out + m * N + n) = o;
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int WF = 0>
 hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
-                      hipStream_t st, int splits = 1, int kps = 0, float* part = nullptr) {
+                      hipStream_t st, int splits = 1, int kps = 0, float* part = nullptr,
+                      const uint8_t* wexp = nullptr) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
     // two ring stages, then the epilogue's scales (row, column and three gate rows)
-    const size_t shm = (size_t)2 * (BM + BN) * kBK + (size_t)(BM + 4 * BN) * 4;
-    auto kern = gemm_fp8_kernel<BM, BN, EPI>;
+    const size_t shm = GemmLds<BM, BN, EPI, WF>::BYTES;
+    auto kern = gemm_fp8_kernel<BM, BN, EPI, WF>;
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(ntm * ntn * splits), dim3(256), shm, st, a, sa, w, sw, out, resid, gate, gate_stride,
-                       M, N, K, L, ntm, ntn, kps, part);
+    hipLaunchKernelGGL(kern, dim3(ntm * ntn * splits), dim3(256), shm, st, a, sa, w, sw, wexp, out, resid, gate,
+                       gate_stride, M, N, K, L, ntm, ntn, kps, part);
     return hipGetLastError();
 }
 
@@ -323,10 +384,10 @@ inline double tile_cost(int M, int N, int BM, int BN, double eff) {
     return (double)((tiles + 255) / 256) * BM * BN / eff;
 }
 
-template <int EPI>
+template <int EPI, int WF = 0>
 hipError_t launch_epi(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
-                      hipStream_t st) {
+                      hipStream_t st, const uint8_t* wexp = nullptr) {
     // the cheapest of the tile shapes that divide N (256 x 192 for the gated residual only)
     double best = 1e300;
     int cfg = 3;
@@ -339,13 +400,17 @@ hipError_t launch_epi(const uint8_t* a, const float* sa, const uint8_t* w, const
     if (c128 < best) best = c128, cfg = 2;
     if (c64 < best) best = c64, cfg = 3;
     switch (cfg) {
-        case 0: return launch_cfg<256, 256, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+        case 0: return launch_cfg<256, 256, EPI, WF>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, 1, 0,
+                                                  nullptr, wexp);
         case 1:
             if constexpr (EPI == SFM_EPI_RESID_GATE)
-                return launch_cfg<256, 192, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+                return launch_cfg<256, 192, EPI, WF>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, 1, 0,
+                                                  nullptr, wexp);
             return hipErrorInvalidValue;
-        case 2: return launch_cfg<256, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
-        default: return launch_cfg<128, 128, EPI>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+        case 2: return launch_cfg<256, 128, EPI, WF>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, 1, 0,
+                                                  nullptr, wexp);
+        default: return launch_cfg<128, 128, EPI, WF>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, 1, 0,
+                                                  nullptr, wexp);
     }
 }
 
@@ -388,6 +453,24 @@ hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uin
             return launch_epi<SFM_EPI_RESID_GATE>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
         case SFM_EPI_SWIGLU:
             return launch_epi<SFM_EPI_SWIGLU>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_mx(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const uint8_t* wexp,
+                          uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
+                          int K, int L, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    switch (epi) {
+        case SFM_EPI_STORE:
+            return launch_epi<SFM_EPI_STORE, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st, wexp);
+        case SFM_EPI_RESID_GATE:
+            return launch_epi<SFM_EPI_RESID_GATE, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st,
+                                                     wexp);
+        case SFM_EPI_SWIGLU:
+            return launch_epi<SFM_EPI_SWIGLU, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st,
+                                                 wexp);
         default:
             return hipErrorInvalidValue;
     }

@@ -74,6 +74,37 @@ __global__ void dequant_fp8_kernel(const uint8_t* __restrict__ q, const float* _
     }
 }
 
+// MXFP4: w = e2m1(q) * 2^(e - 127) for the E8M0 exponent e of the 32-element block; 8 weights
+// (4 bytes, element 2i in the low nibble) per thread.  E2M1: sign, 2 exponent bits (bias 1,
+// 0 = subnormal halves), 1 mantissa bit.  The product is exact (ldexp of a 2-bit significand).
+__global__ void dequant_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ ex, void* out,
+                                  int out_bf16, int n, int k) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i >= (int64_t)n * k) return;
+    const int sh = (int)ex[i / 32] - 127;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(q + i / 2);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t c = (w >> (4 * e)) & 15u;
+        const uint32_t ee = (c >> 1) & 3u, m = c & 1u;
+        const float mag = ee == 0 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)ee - 1);
+        v[e] = __builtin_ldexpf((c & 8u) ? -mag : mag, sh);
+    }
+    if (out_bf16) {
+        uint4 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        o.z = pack_bf16x2(v[4], v[5]);
+        o.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + i) = o;
+    } else {
+        float* f = reinterpret_cast<float*>(out) + i;
+        *reinterpret_cast<float4*>(f) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(f + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 // NF4: w = fp32(code[q] * absmax[block of 64]); 8 weights (4 bytes) per thread.
 __global__ void dequant_nf4_kernel(const uint8_t* __restrict__ q, const float* __restrict__ absmax, Nf4Code code,
                                    void* out, int out_bf16, int n, int k) {
@@ -275,6 +306,15 @@ hipError_t launch_dequant_fp8(const uint8_t* q, const float* s, void* out, int o
     const int64_t threads = ((int64_t)n * k) / 8;
     if (threads == 0) return hipSuccess;
     hipLaunchKernelGGL(dequant_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, q, s, out,
+                       out_bf16, n, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* ex, void* out, int out_bf16, int n, int k,
+                             hipStream_t st) {
+    const int64_t threads = (int64_t)n * k / 8;
+    if (threads == 0) return hipSuccess;
+    hipLaunchKernelGGL(dequant_mx_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, q, ex, out,
                        out_bf16, n, k);
     return hipGetLastError();
 }

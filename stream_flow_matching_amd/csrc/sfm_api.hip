@@ -177,15 +177,19 @@ int check_qweight(const sfm_qweight* w, int fmt, int n, int k, const char* name)
     return SFM_OK;
 }
 
+// *fmt_out: the format of the block's activations path, FP8 (FP8 or mixed weights) or NF4
 int check_block_weights(const sfm_dims* d, const sfm_block_weights* w, int* fmt_out) {
     if (!w) return fail(SFM_E_INVALID_ARG, "block weights are NULL");
     const int fmt = w->qkv.fmt;
-    if (fmt != SFM_W_FP8_E4M3 && fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format %d", fmt);
+    if (fmt != SFM_W_FP8_E4M3 && fmt != SFM_W_NF4_B64)
+        return fail(SFM_E_INVALID_ARG, "unknown weight format %d for qkv", fmt);
+    // mixed: the FFN weights may be MXFP4 when the attention projections are FP8
+    const int ffn = fmt == SFM_W_FP8_E4M3 && w->gate_up.fmt == SFM_W_MXFP4 ? SFM_W_MXFP4 : fmt;
     const int D = d->emb_dim, F = d->intermediate;
     SFM_CHECK(check_qweight(&w->qkv, fmt, 3 * D, D, "qkv"));
     SFM_CHECK(check_qweight(&w->o, fmt, D, D, "o"));
-    SFM_CHECK(check_qweight(&w->gate_up, fmt, 2 * F, D, "gate_up"));
-    SFM_CHECK(check_qweight(&w->down, fmt, D, F, "down"));
+    SFM_CHECK(check_qweight(&w->gate_up, ffn, 2 * F, D, "gate_up"));
+    SFM_CHECK(check_qweight(&w->down, ffn, D, F, "down"));
     SFM_CHECK(check_ptr(w->q_norm, "q_norm"));
     SFM_CHECK(check_ptr(w->k_norm, "k_norm"));
     SFM_CHECK(check_ptr(w->mod_w, "mod_w"));
@@ -197,12 +201,15 @@ int check_block_weights(const sfm_dims* d, const sfm_block_weights* w, int* fmt_
 hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa, const sfm_qweight* w, uint16_t* out,
                 const uint16_t* resid, const float* gate, int64_t gs, int M, int L, hipStream_t st) {
     if (w->fmt == SFM_W_FP8_E4M3)
-        return launch_gemm_fp8(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, w->scale, out, resid, gate, gs, M,
-                               w->n, w->k, L, st);
+        return launch_gemm_fp8(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, (const float*)w->scale, out, resid,
+                               gate, gs, M, w->n, w->k, L, st);
+    if (w->fmt == SFM_W_MXFP4)
+        return launch_gemm_mx(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, (const uint8_t*)w->scale, out, resid,
+                              gate, gs, M, w->n, w->k, L, st);
     Nf4Code code;
     memcpy(code.v, ctx->nf4_code, sizeof code.v);
-    return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, w->scale, code, out, resid, gate, gs, M,
-                           w->n, w->k, L, st);
+    return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, (const float*)w->scale, code, out, resid,
+                           gate, gs, M, w->n, w->k, L, st);
 }
 
 #define SFM_LAUNCH(expr)                                                                              \
@@ -302,7 +309,10 @@ int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
     for (int i = 0; i < mw->num_layers; ++i) {
         int fmt = 0;
         SFM_CHECK(check_block_weights(d, &mw->blocks[i], &fmt));
-        if (fmt != SFM_W_FP8_E4M3) return fail(SFM_E_INVALID_ARG, "layer %d: the velocity model takes FP8 blocks", i);
+        if (fmt != SFM_W_FP8_E4M3)
+            return fail(SFM_E_INVALID_ARG, "layer %d: the velocity model takes FP8 or mixed FP8 / MXFP4 blocks", i);
+        if (mw->blocks[i].gate_up.fmt != mw->blocks[0].gate_up.fmt)
+            return fail(SFM_E_INVALID_ARG, "layer %d: every block must use the FFN weight format of layer 0", i);
     }
     const void* ps[] = {mw->x_w, mw->x_b, mw->t_w1, mw->t_b1, mw->t_w2, mw->t_b2, mw->f_mod_w, mw->f_mod_b, mw->f_w, mw->f_b};
     const char* names[] = {"x_w", "x_b", "t_w1", "t_b1", "t_w2", "t_b2", "f_mod_w", "f_mod_b", "f_w", "f_b"};
@@ -310,25 +320,34 @@ int check_model_weights(const sfm_dims* d, const sfm_model_weights* mw) {
     return SFM_OK;
 }
 
-// One block's FP8 weights laid out in a device slot of the streamed-weights
-// ring (256-byte aligned pieces); fills *w with pointers into base (sizes only
-// when base is NULL) and returns the slot's bytes.
-size_t plan_slot(const sfm_dims* d, char* base, sfm_block_weights* w) {
+// Bytes of a weight's codes and of its scales in format fmt (FP8 or MXFP4).
+size_t qweight_code_bytes(int fmt, int64_t n, int64_t k) { return (size_t)(fmt == SFM_W_MXFP4 ? n * k / 2 : n * k); }
+size_t qweight_scale_bytes(int fmt, int64_t n, int64_t k) { return (size_t)(fmt == SFM_W_MXFP4 ? n * k / 32 : 4 * n); }
+
+// One block's weights laid out in a device slot of the streamed-weights ring
+// (256-byte aligned pieces): qkv and o FP8, gate_up and down in format ffn
+// (FP8 or MXFP4).  Each weight gets the room of its FP8 form, which also holds
+// its MXFP4 form (k/2 + k/32 bytes per row against k + 4), so the slot's size
+// does not depend on ffn.  Fills *w with pointers into base (sizes only when
+// base is NULL) and returns the slot's bytes.
+size_t plan_slot(const sfm_dims* d, char* base, sfm_block_weights* w, int ffn = SFM_W_FP8_E4M3) {
     const int64_t D = d->emb_dim, F = d->intermediate, A = d->adaln_dim;
     Carve c(base);
-    auto qw = [&](int64_t n, int64_t k) {
+    auto qw = [&](int fmt, int64_t n, int64_t k) {
         sfm_qweight q;
-        q.fmt = SFM_W_FP8_E4M3;
+        q.fmt = fmt;
         q.n = (int32_t)n;
         q.k = (int32_t)k;
-        q.q = c.take<uint8_t>((size_t)(n * k));
-        q.scale = c.take<float>((size_t)n);
+        uint8_t* region = c.take<uint8_t>(qweight_code_bytes(SFM_W_FP8_E4M3, n, k) +
+                                          qweight_scale_bytes(SFM_W_FP8_E4M3, n, k));
+        q.q = region;
+        q.scale = region ? region + qweight_code_bytes(fmt, n, k) : nullptr;
         return q;
     };
-    w->qkv = qw(3 * D, D);
-    w->o = qw(D, D);
-    w->gate_up = qw(2 * F, D);
-    w->down = qw(D, F);
+    w->qkv = qw(SFM_W_FP8_E4M3, 3 * D, D);
+    w->o = qw(SFM_W_FP8_E4M3, D, D);
+    w->gate_up = qw(ffn, 2 * F, D);
+    w->down = qw(ffn, D, F);
     w->q_norm = c.take<uint16_t>(256);
     w->k_norm = c.take<uint16_t>(256);
     w->mod_w = c.take<uint16_t>((size_t)(4 * D * A));
@@ -346,8 +365,10 @@ hipError_t stage_block(const sfm_dims* d, const sfm_block_weights* src, const sf
     } pieces[] = {
         {dst->qkv.q, src->qkv.q, (size_t)(3 * D * D)},        {dst->qkv.scale, src->qkv.scale, (size_t)(3 * D * 4)},
         {dst->o.q, src->o.q, (size_t)(D * D)},                {dst->o.scale, src->o.scale, (size_t)(D * 4)},
-        {dst->gate_up.q, src->gate_up.q, (size_t)(2 * F * D)}, {dst->gate_up.scale, src->gate_up.scale, (size_t)(2 * F * 4)},
-        {dst->down.q, src->down.q, (size_t)(D * F)},          {dst->down.scale, src->down.scale, (size_t)(D * 4)},
+        {dst->gate_up.q, src->gate_up.q, qweight_code_bytes(src->gate_up.fmt, 2 * F, D)},
+        {dst->gate_up.scale, src->gate_up.scale, qweight_scale_bytes(src->gate_up.fmt, 2 * F, D)},
+        {dst->down.q, src->down.q, qweight_code_bytes(src->down.fmt, D, F)},
+        {dst->down.scale, src->down.scale, qweight_scale_bytes(src->down.fmt, D, F)},
         {dst->q_norm, src->q_norm, 512},                      {dst->k_norm, src->k_norm, 512},
         {dst->mod_w, src->mod_w, (size_t)(4 * D * A * 2)},    {dst->mod_b, src->mod_b, (size_t)(4 * D * 4)},
     };
@@ -406,8 +427,9 @@ int run_model_streamed(const sfm_context* ctx, const sfm_model_weights* mw, cons
     Carve c(ws);
     char* model_ws = c.take<char>(plan_model(d, B, T, gh, gw, nullptr).bytes);
     sfm_block_weights slot[2];
-    const size_t slot_bytes = plan_slot(d, nullptr, &slot[0]);
-    for (int s = 0; s < 2; ++s) plan_slot(d, c.take<char>(slot_bytes), &slot[s]);
+    const int ffn = mw->num_layers > 0 ? mw->blocks[0].gate_up.fmt : SFM_W_FP8_E4M3;
+    const size_t slot_bytes = plan_slot(d, nullptr, &slot[0], ffn);
+    for (int s = 0; s < 2; ++s) plan_slot(d, c.take<char>(slot_bytes), &slot[s], ffn);
     StepWs w = plan_model(d, B, T, gh, gw, model_ws);
     const int n = mw->num_layers;
     std::lock_guard<std::mutex> guard(cx->step_lock);
@@ -636,13 +658,14 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     if (epi < SFM_EPI_STORE || epi > SFM_EPI_SWIGLU) return fail(SFM_E_INVALID_ARG, "unknown epilogue %d", epi);
     if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
-    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format");
+    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64 && w->fmt != SFM_W_MXFP4)
+        return fail(SFM_E_INVALID_ARG, "unknown weight format");
     SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
     if (w->n < 256 || w->n % 256 || w->k < 256 || w->k % 256)
         return fail(SFM_E_SHAPE, "weight [%d][%d]: need n %% 256 == 0 and k %% 256 == 0", w->n, w->k);
     SFM_CHECK(check_ptr(a, "a"));
     SFM_CHECK(check_ptr(out, "out"));
-    if (w->fmt == SFM_W_FP8_E4M3 && !a_scale) return fail(SFM_E_INVALID_ARG, "a_scale is NULL");
+    if (w->fmt != SFM_W_NF4_B64 && !a_scale) return fail(SFM_E_INVALID_ARG, "a_scale is NULL");
     if (M < 0 || L < 1) return fail(SFM_E_SHAPE, "M >= 0 and L >= 1 required");
     if (epi == SFM_EPI_RESID_GATE) {
         SFM_CHECK(check_ptr(resid, "resid"));
@@ -691,11 +714,11 @@ int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* n
     // a prompt has few rows and the features are long: split K when the output tiles alone would
     // leave most of the compute units idle
     if (parts > 1)
-        SFM_LAUNCH(launch_gemm_fp8_splitk(codes, scales, (const uint8_t*)proj->q, proj->scale, text_out, M, D, K, part,
-                                          st));
+        SFM_LAUNCH(launch_gemm_fp8_splitk(codes, scales, (const uint8_t*)proj->q, (const float*)proj->scale, text_out,
+                                          M, D, K, part, st));
     else
-        SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, proj->scale, text_out,
-                                   nullptr, nullptr, 0, M, D, K, M, st));
+        SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, (const float*)proj->scale,
+                                   text_out, nullptr, nullptr, 0, M, D, K, M, st));
     return SFM_OK;
 }
 
@@ -771,18 +794,22 @@ int sfm_euler_cfg(const float* z, const float* v_c, const float* v_u, float* z_o
 int sfm_dequant(const sfm_context* ctx, const sfm_qweight* w, void* out, int out_dtype, void* stream) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
-    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64) return fail(SFM_E_INVALID_ARG, "unknown weight format");
+    if (w->fmt != SFM_W_FP8_E4M3 && w->fmt != SFM_W_NF4_B64 && w->fmt != SFM_W_MXFP4)
+        return fail(SFM_E_INVALID_ARG, "unknown weight format");
     SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
     SFM_CHECK(check_ptr(out, "out"));
     if (out_dtype != 0 && out_dtype != 1) return fail(SFM_E_INVALID_ARG, "out_dtype must be 0 (fp32) or 1 (bf16)");
     if (w->n < 1 || w->k < 64 || w->k % 64) return fail(SFM_E_SHAPE, "k must be a positive multiple of 64");
     const hipStream_t st = (hipStream_t)stream;
     if (w->fmt == SFM_W_FP8_E4M3) {
-        SFM_LAUNCH(launch_dequant_fp8((const uint8_t*)w->q, w->scale, out, out_dtype, w->n, w->k, st));
+        SFM_LAUNCH(launch_dequant_fp8((const uint8_t*)w->q, (const float*)w->scale, out, out_dtype, w->n, w->k, st));
+    } else if (w->fmt == SFM_W_MXFP4) {
+        SFM_LAUNCH(launch_dequant_mx((const uint8_t*)w->q, (const uint8_t*)w->scale, out, out_dtype, w->n, w->k, st));
     } else {
         Nf4Code code;
         memcpy(code.v, ctx->nf4_code, sizeof code.v);
-        SFM_LAUNCH(launch_dequant_nf4((const uint8_t*)w->q, w->scale, code, out, out_dtype, w->n, w->k, st));
+        SFM_LAUNCH(launch_dequant_nf4((const uint8_t*)w->q, (const float*)w->scale, code, out, out_dtype, w->n, w->k,
+                                      st));
     }
     return SFM_OK;
 }

@@ -167,6 +167,11 @@ hipError_t launch_timestep_embed(float t, float* e, int B, int dim, hipStream_t 
 hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
                            int K, int L, hipStream_t st);
+// MXFP4 weights: w packed E2M1 nibbles [N][K/2] (element 2i in the low nibble), wexp E8M0
+// exponents [N][K/32]; FP8 activation codes as for launch_gemm_fp8; K % 256 == 0
+hipError_t launch_gemm_mx(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const uint8_t* wexp,
+                          uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
+                          int K, int L, hipStream_t st);
 // Split-K FP8 STORE projection for few rows and long K (few output tiles): splitk_parts(M, N, K)
 // parts of fp32 partial sums in `part` ([parts][M][N]), then a reduce applying sa, sw and the
 // bf16 rounding.  1 part means the plain launch would fill the chip as well.
@@ -201,6 +206,8 @@ hipError_t launch_euler_cfg(const float* z, const float* vc, const float* vu, fl
                             float g, float dt, hipStream_t st);
 hipError_t launch_dequant_fp8(const uint8_t* q, const float* s, void* out, int out_bf16, int n, int k,
                               hipStream_t st);
+hipError_t launch_dequant_mx(const uint8_t* q, const uint8_t* ex, void* out, int out_bf16, int n, int k,
+                             hipStream_t st);
 hipError_t launch_dequant_nf4(const uint8_t* q, const float* absmax, const Nf4Code& code, void* out, int out_bf16,
                               int n, int k, hipStream_t st);
 // out[m][n] = sum_k a[m][k] w[n][k] + bias[n]; a fp32 or bf16, w bf16, out bf16 or fp32.

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libsfm.so")
 
 SFM_W_FP8_E4M3 = 1
 SFM_W_NF4_B64 = 2
+SFM_W_MXFP4 = 3
 SFM_EPI_STORE = 0
 SFM_EPI_RESID_GATE = 1
 SFM_EPI_SWIGLU = 2
@@ -177,7 +178,7 @@ class Context:
 
 def qweight(fmt, q, scale):
     n = q.shape[0]
-    k = q.shape[1] * (2 if fmt == SFM_W_NF4_B64 else 1)
+    k = q.shape[1] * (2 if fmt in (SFM_W_NF4_B64, SFM_W_MXFP4) else 1)
     return sfm_qweight(fmt, n, k, q.data_ptr(), scale.data_ptr())
 
 
@@ -185,10 +186,12 @@ class BlockWeights:
     """sfm_block_weights over device tensors (keeps them alive)."""
 
     def __init__(self, p):
-        fmt = SFM_W_FP8_E4M3 if p.fmt == "fp8" else SFM_W_NF4_B64
+        # "mixed": qkv and o FP8, gate_up and down MXFP4 (the activations path is the FP8 one)
+        fmt = SFM_W_FP8_E4M3 if p.fmt in ("fp8", "mixed") else SFM_W_NF4_B64
+        ffn = SFM_W_MXFP4 if p.fmt == "mixed" else fmt
         self._keep = p
-        self.c = sfm_block_weights(qweight(fmt, *p.qkv), qweight(fmt, *p.o), qweight(fmt, *p.gate_up),
-                                   qweight(fmt, *p.down), p.q_norm.data_ptr(), p.k_norm.data_ptr(),
+        self.c = sfm_block_weights(qweight(fmt, *p.qkv), qweight(fmt, *p.o), qweight(ffn, *p.gate_up),
+                                   qweight(ffn, *p.down), p.q_norm.data_ptr(), p.k_norm.data_ptr(),
                                    p.mod_w.data_ptr(), p.mod_b.data_ptr())
         self.fmt = fmt
 

@@ -20,10 +20,14 @@ quantisation section; NF4 block 64 per its NF4 subsection):
     an extreme level (+-1, the absmax element), absmax = max |N(0, 0.02**2)|
     over 64 draws.
   * MXFP4 (the 4-bit FFN layers of the mixed scheme, deployment post section
-    2.2): E2M1 codes uniform over the 16 levels, one element per 32-block
-    forced to +-6 (the block maximum), E8M0 exponents uniform in 119..121 (the
-    block scales N(0, 0.02**2) weights give).  The "mixed" block keeps QKV and
-    the output projection in FP8 and puts gate/up and down in MXFP4.
+    2.2): the code and scale frequencies that OCP MX quantisation of
+    N(0, 0.02**2) weights produces (tables below, worked out offline from the
+    normal distribution): each 32-block draws its E8M0 exponent (119, 120, 121
+    with probability 0.0179, 0.9268, 0.0553), each element a magnitude code
+    0..7 from that exponent's row and a random sign, and one element per block
+    is forced to +-6 (the block maximum).  Weight rms 0.020, as for FP8.  The
+    "mixed" block keeps QKV and the output projection in FP8 and puts gate/up
+    and down in MXFP4.
   * small layers (latent embed, timestep MLP, final layer): N(0, 1/fan_in) in
     bf16; modulation weights N(0, 0.02**2) bf16 with zero bias; QK-norm
     weights 1 + N(0, 0.02**2) in bf16.
@@ -100,6 +104,14 @@ def nf4_weight(n, k, key, std=0.02, device="cpu"):
     return packed, absmax
 
 
+# MXFP4 recipe tables: block exponents 119, 120, 121 and, per exponent, the
+# frequencies of the magnitude codes 0..7
+_MX_EXP_P = (0.0179, 0.9268, 0.0553)
+_MX_CODE_P = ((0.0389, 0.0775, 0.0764, 0.0746, 0.1072, 0.1311, 0.1654, 0.3289),
+              (0.0778, 0.1527, 0.1442, 0.1311, 0.1654, 0.1572, 0.1208, 0.0508),
+              (0.1549, 0.2872, 0.2291, 0.1572, 0.1208, 0.0446, 0.0061, 0.0001))
+
+
 def mxfp4_weight(n, k, key, device="cpu"):
     """(packed uint8 [n, k/2], exponents uint8 [n, k/32]) per the MXFP4 recipe above.
 
@@ -108,12 +120,22 @@ def mxfp4_weight(n, k, key, device="cpu"):
     if k % 32:
         raise ValueError("k must be a multiple of 32 for MXFP4 blocks")
     g = _gen(key + ("codes",), device)
-    q = torch.randint(0, 16, (n, k), generator=g, device=device, dtype=torch.int32)
     nb = n * k // 32
+    ue = torch.rand(nb, generator=g, device=device)
+    ei = (ue >= _MX_EXP_P[0]).to(torch.int32) + (ue >= _MX_EXP_P[0] + _MX_EXP_P[1]).to(torch.int32)
+    cdf = torch.tensor(np.cumsum(_MX_CODE_P, axis=1)[:, :7], dtype=torch.float32, device=device)
+    rows = cdf[ei.long()]                                   # [nb, 7]
+    u = torch.rand(nb, 32, generator=g, device=device)
+    q = torch.zeros(nb, 32, dtype=torch.int32, device=device)
+    for j in range(7):
+        q += (u >= rows[:, j:j + 1]).to(torch.int32)
+    q = q.view(n, k)
+    del rows, u
+    q += 8 * torch.randint(0, 2, (n, k), generator=g, device=device, dtype=torch.int32)
     where = torch.randint(0, 32, (nb,), generator=g, device=device)
     ext = torch.where(torch.rand(nb, generator=g, device=device) < 0.5, 7, 15).to(torch.int32)
     q.view(nb, 32).scatter_(1, where[:, None], ext[:, None])
-    e = torch.randint(119, 122, (n, k // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    e = (119 + ei).view(n, k // 32).to(torch.uint8)
     packed = (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8).contiguous()
     return packed, e.contiguous()
 
@@ -230,10 +252,11 @@ class ModelParams:
     f_b: torch.Tensor
 
 
-def model_params(shape: Shape, layers, key, device="cpu") -> ModelParams:
+def model_params(shape: Shape, layers, key, device="cpu", fmt="fp8") -> ModelParams:
+    """fmt: the blocks' weight format, "fp8" or "mixed"."""
     D, A, C = shape.emb_dim, shape.adaln_dim, shape.latent_ch
     return ModelParams(
-        blocks=[block_params(shape, key + ("layer", i), "fp8", device) for i in range(layers)],
+        blocks=[block_params(shape, key + ("layer", i), fmt, device) for i in range(layers)],
         x_w=bf16_normal((D, C), key + ("x_w",), C ** -0.5, device=device),
         x_b=randn((D,), key + ("x_b",), 0.02, device),
         t_w1=bf16_normal((A, A), key + ("t_w1",), A ** -0.5, device=device),

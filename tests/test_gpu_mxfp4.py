@@ -1,0 +1,221 @@
+"""GPU parity of the MXFP4 weights (E2M1 elements, E8M0 scale per 32 elements)
+and of the mixed block (QKV and output projection FP8, gate/up and down MXFP4;
+deployment post, section 2.2), through the C entry points, against the oracle.
+
+Bars as in test_gpu_parity.py: dequantisation bit-exact; projections within
+rel-L2 2e-3; blocks within 1e-2 and their update within the FP8 bar (the
+activations are quantised per token to E4M3 exactly as for FP8 weights)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dit as O
+from oracle import numerics as N
+from stream_flow_matching_amd import synth
+from tests._util import np64, npu8, oracle_block, rel_l2, to_device
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+UPDATE_BAR = 2.5e-2
+
+
+def _say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sfm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from stream_flow_matching_amd import sfm as S
+    S.lib()
+    return S
+
+
+@pytest.fixture(scope="module")
+def ctx_tiny(sfm):
+    return sfm.Context("tiny")
+
+
+@pytest.fixture(scope="module")
+def ctx_full(sfm):
+    return sfm.Context("ideogram4")
+
+
+@pytest.mark.parametrize("n,k", [(1536, 512), (8, 128)])
+def test_dequant_mxfp4_bit_exact(sfm, ctx_tiny, n, k):
+    """All 16 codes and exponents from the subnormal end (0, 1) to 252."""
+    _say("dequant mxfp4", n, k)
+    packed, ex = synth.mxfp4_weight(n, k, ("dqmx", n, k))
+    packed.view(-1)[:8] = torch.tensor([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], dtype=torch.uint8)
+    ex.view(-1)[:6] = torch.tensor([0, 1, 126, 127, 200, 252], dtype=torch.uint8)
+    keep = (packed.to(DEV), ex.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_MXFP4, *keep)
+    out = torch.empty(n, k, dtype=torch.float32, device=DEV)
+    outb = torch.empty(n, k, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_dequant(ctx_tiny, w, out)
+    sfm.sfm_dequant(ctx_tiny, w, outb)
+    torch.cuda.synchronize()
+    ref = N.mxfp4_dequant_f32(npu8(packed), npu8(ex), n, k)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(np64(outb), N.bf16_round(ref.astype(np.float64)))
+
+
+def _rand_codes(shape, key):
+    g = torch.Generator().manual_seed(synth.seed_of(*key))
+    c = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    c[c == 0x7F] = 0x7E
+    c[c == 0xFF] = 0xFE
+    return c
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2])
+@pytest.mark.parametrize("M", [272, 128, 37])
+def test_linear_mxfp4(sfm, ctx_tiny, epi, M):
+    """FP8 activation codes x MXFP4 weights with each epilogue, ragged M."""
+    _say("linear mxfp4", epi, M)
+    K, Nw, L = 512, 1536, 136 if M > 136 else M
+    a = _rand_codes((M, K), ("lmx", M, epi))
+    sa = (torch.rand(M, generator=torch.Generator().manual_seed(2)) * 0.01 + 1e-3).float()
+    packed, ex = synth.mxfp4_weight(Nw, K, ("lmxw", epi))
+    keep = (packed.to(DEV), ex.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_MXFP4, *keep)
+    Bn = (M + L - 1) // L
+    wd = N.mxfp4_dequant_f32(npu8(packed), npu8(ex), Nw, K).astype(np.float64)
+    y = (N.e4m3_decode(npu8(a)) @ wd.T) * sa.numpy()[:, None].astype(np.float64)
+    if epi == 2:
+        out = torch.empty(M, Nw // 2, dtype=torch.bfloat16, device=DEV)
+        sfm.sfm_linear(ctx_tiny, epi, a.to(DEV), sa.to(DEV), w, out, M=M, L=L)
+        ref = N.bf16_round(O.silu(y[:, :Nw // 2]) * y[:, Nw // 2:])
+    else:
+        resid = synth.bf16_normal((M, Nw), ("lmxr", M), 1.0)
+        gate = synth.randn((Bn, Nw), ("lmxg", M), 0.5)
+        out = torch.empty(M, Nw, dtype=torch.bfloat16, device=DEV)
+        if epi == 0:
+            sfm.sfm_linear(ctx_tiny, epi, a.to(DEV), sa.to(DEV), w, out, M=M, L=L)
+            ref = N.bf16_round(y)
+        else:
+            sfm.sfm_linear(ctx_tiny, epi, a.to(DEV), sa.to(DEV), w, out, resid.to(DEV), gate.to(DEV), Nw, M=M, L=L)
+            ref = N.bf16_round(np64(resid) + np64(gate)[np.arange(M) // L] * y)
+    torch.cuda.synchronize()
+    got = np64(out)
+    assert rel_l2(got, ref) < 2e-3
+    if epi == 1:
+        assert rel_l2(got - np64(resid), ref - np64(resid)) < 1e-2
+
+
+def test_linear_mxfp4_full_width_sampled(sfm, ctx_full):
+    """The 1024^2 gate/up projection (M 4608, N 24576, K 4608, SwiGLU) and the down
+    projection (N 4608, K 12288, gated residual in place) in MXFP4: sampled rows."""
+    _say("linear mxfp4 full")
+    rows = np.array([0, 1, 255, 256, 2047, 4095, 4607])
+    M, D, F = 4608, 4608, 12288
+    a = _rand_codes((M, D), ("lmxf",))
+    sa = (torch.rand(M, generator=torch.Generator().manual_seed(3)) * 2e-3 + 5e-4).float()
+    packed, ex = synth.mxfp4_weight(2 * F, D, ("lmxf_gu",))
+    keep = (packed.to(DEV), ex.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_MXFP4, *keep)
+    out = torch.empty(M, F, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_linear(ctx_full, 2, a.to(DEV), sa.to(DEV), w, out, M=M, L=M)
+    torch.cuda.synchronize()
+    wd = N.mxfp4_dequant_f32(npu8(packed), npu8(ex), 2 * F, D).astype(np.float64)
+    y = (N.e4m3_decode(npu8(a[rows])) @ wd.T) * sa.numpy()[rows, None].astype(np.float64)
+    ref = N.bf16_round(O.silu(y[:, :F]) * y[:, F:])
+    assert rel_l2(np64(out[rows]), ref) < 2e-3
+    del keep, w, out, wd
+    # down projection: K 12288, gated residual in place, three batches of L 1536
+    a2 = _rand_codes((M, F), ("lmxf2",))
+    packed2, ex2 = synth.mxfp4_weight(D, F, ("lmxf_dn",))
+    keep2 = (packed2.to(DEV), ex2.to(DEV))
+    w2 = sfm.qweight(sfm.SFM_W_MXFP4, *keep2)
+    L = 1536
+    resid = synth.bf16_normal((M, D), ("lmxf2r",), 1.0)
+    gate = synth.randn((M // L, D), ("lmxf2g",), 0.5)
+    x = resid.to(DEV)
+    sfm.sfm_linear(ctx_full, 1, a2.to(DEV), sa.to(DEV), w2, x, x, gate.to(DEV), D, M=M, L=L)
+    torch.cuda.synchronize()
+    wd2 = N.mxfp4_dequant_f32(npu8(packed2), npu8(ex2), D, F).astype(np.float64)
+    y2 = (N.e4m3_decode(npu8(a2[rows])) @ wd2.T) * sa.numpy()[rows, None].astype(np.float64)
+    ref2 = N.bf16_round(np64(resid[rows]) + np64(gate)[rows // L] * y2)
+    got2 = np64(x[rows])
+    assert rel_l2(got2, ref2) < 2e-3
+    assert rel_l2(got2 - np64(resid[rows]), ref2 - np64(resid[rows])) < 1e-2
+
+
+def _run_block(sfm, ctx, w, p, x, c):
+    B, L, D = x.shape
+    bw = sfm.BlockWeights(to_device(p))
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx, B, w.T, w.gh, w.gw, bw.fmt))
+    xo = torch.empty(B, L, D, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_block_forward(ctx, bw, x.to(DEV), xo, c.to(DEV), B, w.T, w.gh, w.gw, ws)
+    torch.cuda.synchronize()
+    return xo
+
+
+def test_block_mixed_tiny(sfm, ctx_tiny):
+    _say("block mixed tiny")
+    w = synth.Workload("tiny_mixed", synth.TINY, 2, 16, 16, 17)
+    p = synth.block_params(w.shape, (0, w.name), "mixed")
+    x, c = synth.block_inputs(w)
+    xo = _run_block(sfm, ctx_tiny, w, p, x, c)
+    ref = O.block_forward(np64(x), c.numpy().astype(np.float64), oracle_block(p), w.T, w.gh, w.gw, O.TINY)
+    got = np64(xo)
+    assert rel_l2(got, ref) < 1e-2
+    assert rel_l2(got - np64(x), ref - np64(x)) < UPDATE_BAR
+
+
+def test_block_mixed_full_sampled(sfm, ctx_full):
+    """The full-width 1024^2 block (512 text + 64x64 image tokens) with mixed weights."""
+    _say("block mixed full")
+    w = synth.Workload("full_mixed", synth.FULL, 1, 512, 64, 64)
+    p = synth.block_params(w.shape, (0, w.name), "mixed")
+    x, c = synth.block_inputs(w)
+    xo = _run_block(sfm, ctx_full, w, p, x, c)
+    M = w.L
+    rows = np.unique(np.r_[0, w.T - 1, w.T, w.L - 1, np.linspace(0, M - 1, 12).astype(int)])
+    ref = O.block_forward(np64(x), c.numpy().astype(np.float64), oracle_block(p), w.T, w.gh, w.gw, O.IDEOGRAM4,
+                          rows=rows)
+    got = np64(xo).reshape(M, -1)[rows]
+    xin = np64(x).reshape(M, -1)[rows]
+    assert rel_l2(got, ref) < 1e-2
+    assert rel_l2(got - xin, ref - xin) < UPDATE_BAR
+
+
+def _pinned(obj):
+    import dataclasses
+    if isinstance(obj, torch.Tensor):
+        return obj.cpu().contiguous().pin_memory()
+    if isinstance(obj, tuple):
+        return tuple(_pinned(x) for x in obj)
+    if dataclasses.is_dataclass(obj):
+        return dataclasses.replace(obj, **{f.name: _pinned(getattr(obj, f.name)) for f in dataclasses.fields(obj)})
+    return obj
+
+
+def test_model_velocity_mixed_streamed_equals_resident(sfm, ctx_tiny):
+    """A 4-layer mixed model: the host-streamed velocity (FFN weights copied in
+    their MXFP4 form) equals the resident one bitwise, two calls in a row."""
+    import dataclasses
+    _say("velocity mixed streamed")
+    w = synth.Workload("mx_str", synth.TINY, 1, 16, 16, 16, layers=4)
+    mp = synth.model_params(w.shape, w.layers, (0, w.name), fmt="mixed")
+    dev = to_device(mp)
+    host = dataclasses.replace(dev, blocks=[_pinned(b) for b in mp.blocks])
+    mw_dev, mw_host = sfm.ModelWeights(dev), sfm.ModelWeights(host)
+    text, z, t, _ = synth.step_inputs(w)
+    ws_r = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw))
+    ws_s = sfm.workspace(sfm.lib().sfm_streamed_workspace_bytes(ctx_tiny.handle, 1, w.T, w.gh, w.gw))
+    for rep in range(2):
+        zz = (z * (1.0 + rep)).to(DEV)
+        tt = t * (0.5 + 0.25 * rep)
+        v_r = torch.empty(1, w.gh * w.gw, 128, device=DEV)
+        v_s = torch.empty_like(v_r)
+        sfm.sfm_model_velocity(ctx_tiny, mw_dev, text.to(DEV), zz, tt, v_r, 1, w.T, w.gh, w.gw, ws_r)
+        sfm.sfm_model_velocity_streamed(ctx_tiny, mw_host, text.to(DEV), zz, tt, v_s, 1, w.T, w.gh, w.gw, ws_s)
+        torch.cuda.synchronize()
+        assert torch.isfinite(v_s).all()
+        assert torch.equal(v_r, v_s)
