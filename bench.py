@@ -115,13 +115,20 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
         el = time.perf_counter() - t0
         samples[name] = {"steps": len(g), "s_per_image": round(el, 4), "ms_per_step": round(el / len(g) * 1e3, 3),
                          "finite": bool(torch.isfinite(zo).all())}
-    streamed = streamed_bench(sfm, ctx, cond, cm, text, z, t, w) if presets else None
-    del cond, unc, cm, um, ws
+    streamed = None
+    if presets:
+        streamed = {"fp8": streamed_bench(sfm, ctx, cond, cm, text, z, t, w)}
+        del cond, unc, cm, um, ws
+        torch.cuda.empty_cache()
+        mixed = synth.model_params(w.shape, w.layers, (0, "cond"), device="cuda", fmt="mixed")
+        streamed["mixed"] = streamed_bench(sfm, ctx, mixed, sfm.ModelWeights(mixed), text, z, t, w,
+                                           weights="QKV and output projection FP8, gate/up and down MXFP4")
+        del mixed
     torch.cuda.empty_cache()
     return sec, ok, launches[:w.layers], launches[w.layers:], samples, streamed
 
 
-def streamed_bench(sfm, ctx, cond, cm, text, z, t, w, iters=2):
+def streamed_bench(sfm, ctx, cond, cm, text, z, t, w, iters=2, weights="FP8"):
     """The conditional velocity pass (34 layers, 1024^2) with its block weights
     in pinned host memory, streamed layer by layer, against the same pass with
     resident weights.  H2D rate = block weight bytes copied per second."""
@@ -149,24 +156,28 @@ def streamed_bench(sfm, ctx, cond, cm, text, z, t, w, iters=2):
               for x in (b.qkv + b.o + b.gate_up + b.down + (b.q_norm, b.k_norm, b.mod_w, b.mod_b)))
     del host, mh, ws_s, ws_r
     return {"workload": "conditional pass, 34 layers at 1024^2, block weights in pinned host memory",
-            "ms_streamed": round(s_str * 1e3, 2), "ms_resident": round(s_res * 1e3, 2),
+            "weights": weights, "ms_streamed": round(s_str * 1e3, 2), "ms_resident": round(s_res * 1e3, 2),
             "block_weight_bytes": blk, "h2d_gb_s": round(blk / s_str / 1e9, 2)}
 
 
-def block_bench(sfm, synth, ctx, name, iters=5):
+def block_bench(sfm, synth, ctx, name, iters=5, fmt=None):
+    """One block at a named workload; fmt overrides its weight format ("mixed":
+    QKV and output projection FP8, gate/up and down MXFP4, priced against the
+    FP8 peak since FP8 x FP4 products run at the FP8 rate)."""
     import torch
     w = synth.WORKLOADS[name]
-    p = synth.block_params(w.shape, (0, w.name), w.wfmt, device="cuda")
+    fmt = fmt or w.wfmt
+    p = synth.block_params(w.shape, (0, w.name), fmt, device="cuda")
     bw = sfm.BlockWeights(p)
     x, c = synth.block_inputs(w, device="cuda")
     xo = torch.empty_like(x)
     ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw, bw.fmt))
     sec = time_gpu(lambda: sfm.sfm_block_forward(ctx, bw, x, xo, c, w.B, w.T, w.gh, w.gw, ws), iters)
     fl = block_flops(w.L, w.B)
-    peak = FP8_PEAK_TFLOPS if w.wfmt == "fp8" else BF16_PEAK_TFLOPS
+    peak = BF16_PEAK_TFLOPS if fmt == "nf4" else FP8_PEAK_TFLOPS
     return {"workload": w.describe, "ms": round(sec * 1e3, 4), "tokens_per_s": round(w.B * w.L / sec, 1),
             "tflops": round(fl / sec / 1e12, 2), "frac_matrix_peak": round(fl / sec / 1e12 / peak, 4),
-            "weights": w.wfmt}
+            "weights": fmt}
 
 
 def block_varlen_bench(sfm, synth, ctx, lens=(512, 77), iters=5):
@@ -227,6 +238,8 @@ def text_project_bench(sfm, synth, ctx, M=512, iters=10):
 
 
 ROOF_SHAPE = (4608, 4608, 12288)   # M, K, F of the dominant launch (gate/up + SwiGLU, conditional pass)
+# its kernel as rocprofv3 names it: tile 256 x 256, SwiGLU epilogue (2), FP8 weights (0)
+DOMINANT = "gemm_fp8_kernel<256, 256, 2, 0>"
 ROOF_SOURCES = ("stream_flow_matching_amd/csrc/k_gemm_fp8.hip", "stream_flow_matching_amd/csrc/gemm_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_swiglu_4608x24576x4608_traffic.md")
 COPY_BYTES = 256 << 20            # plain copy kernel used to calibrate the byte counters
@@ -318,7 +331,7 @@ def pmc_summary(fetch_dir, write_dir):
         for r in csv.DictReader(open(f[0])):
             if r["Counter_Name"] != counter:
                 continue
-            if "gemm_fp8_kernel<256, 256, 2>" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
+            if DOMINANT in r["Kernel_Name"] and int(r["Grid_Size"]) == grid:
                 g.append(float(r["Counter_Value"]))
             elif "copyBuffer" in r["Kernel_Name"]:
                 c.append(float(r["Counter_Value"]))
@@ -385,7 +398,7 @@ def trace_summary(out_dir, layers=34):
         name = short(r["Kernel_Name"])
         groups[(name, wg)].append(us)
         M, _, F = ROOF_SHAPE
-        if name == "gemm_fp8_kernel<256, 256, 2>" and wg == (M // 256) * (2 * F // 256):
+        if name == DOMINANT and wg == (M // 256) * (2 * F // 256):
             dominant.append(us)
     total = sum(sum(v) for v in groups.values())
     print("| kernel | workgroups | launches | avg us | share of GPU time (%) |")
@@ -395,7 +408,7 @@ def trace_summary(out_dir, layers=34):
     if dominant:
         last = dominant[-layers:]
         print()
-        print(f"Dominant launch `gemm_fp8_kernel<256, 256, 2>` at {(ROOF_SHAPE[0] // 256) * (2 * ROOF_SHAPE[2] // 256)} "
+        print(f"Dominant launch `{DOMINANT}` at {(ROOF_SHAPE[0] // 256) * (2 * ROOF_SHAPE[2] // 256)} "
               f"workgroups: {len(dominant)} launches, average {sum(dominant) / len(dominant):.2f} us; "
               f"last {len(last)} (the last step): average {sum(last) / len(last):.2f} us.")
     stats = sorted(glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True))
@@ -470,6 +483,7 @@ def main():
     if not args.no_extra:
         for name in ("block_1024", "block_2048", "block_6to1_nf4"):
             extra[name] = block_bench(sfm, synth, ctx, name)
+        extra["block_1024_mixed"] = block_bench(sfm, synth, ctx, "block_1024", fmt="mixed")
         extra["text_projection_512"] = text_project_bench(sfm, synth, ctx)
         extra["block_1024_varlen_b2"] = block_varlen_bench(sfm, synth, ctx)
         extra["attention_4608"] = attention_bench(sfm, ctx, 4608)

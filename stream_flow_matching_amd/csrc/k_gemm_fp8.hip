@@ -272,8 +272,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int k = 0; k < NSL; ++k)
         if (tid + 256 * k < NSC) scl[tid + 256 * k] = scv[k];
     lds_barrier();
+    // in program order, as the loop reads them: the loop head then waits only for the first
+    // fragments (issued in another order, the first MFMA would need the last read and the
+    // compiler would wait for all of them at the head of every stage)
 #pragma unroll
-    for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
+    for (int f = 0; f < NF; ++f) {
+        ds(0, f, smem, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // stage t: set 0 holds half 0 of stage t on entry and half 0 of stage t + 1 on exit.
     // Barrier A (after the reads of half 1) frees stage t's buffer for the loads of stage
@@ -289,9 +295,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const __amdgpu_buffer_rsrc_t rB = more ? rb : rb0;
         const int k2 = kbeg + (t + 2) * kBK;
         // the next stage's block exponents go out before this stage's loads (the waits below
-        // then cover them)
-        if constexpr (MX)
-            if (t + 1 < nks) load_exp(sn, t + 1);
+        // then cover them); the last stage re-reads its own word, which keeps the loop free of a
+        // branch (a conditional block at the loop head makes the compiler wait for every LDS read
+        // before the first MFMA)
+        if constexpr (MX) load_exp(sn, min(t + 1, nks - 1));
         quarter(0, 0, true, 1, cur, 1, 0, 0, cur, rA, rB, k2);
         wait_vm_lgkm0<63>();
         lds_barrier();
