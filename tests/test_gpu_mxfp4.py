@@ -219,3 +219,57 @@ def test_model_velocity_mixed_streamed_equals_resident(sfm, ctx_tiny):
         torch.cuda.synchronize()
         assert torch.isfinite(v_s).all()
         assert torch.equal(v_r, v_s)
+
+
+def test_mxfp4_argument_checks(sfm, ctx_tiny):
+    """Format and shape rules of MXFP4 weights, all refused on the host before
+    any launch: a block mixes only FP8 attention with MXFP4 FFN (both FFN
+    weights alike), every layer of a model shares layer 0's FFN format, a
+    projection needs n and k multiples of 256 and activation scales,
+    dequantisation k a multiple of 64."""
+    _say("mxfp4 argument checks")
+    w = synth.Workload("mx_args", synth.TINY, 1, 16, 16, 16, layers=2)
+    D, F = w.shape.emb_dim, w.shape.intermediate
+    x, c = synth.block_inputs(w, device=DEV)
+    xo = torch.empty_like(x)
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw, sfm.SFM_W_FP8_E4M3))
+
+    def block_call(bw):
+        sfm.sfm_block_forward(ctx_tiny, bw, x, xo, c, 1, w.T, w.gh, w.gw, ws)
+
+    mixed = synth.block_params(w.shape, (0, "mx_args"), "mixed", device=DEV)
+    fp8 = synth.block_params(w.shape, (1, "mx_args"), "fp8", device=DEV)
+    nf4 = synth.block_params(w.shape, (2, "mx_args"), "nf4", device=DEV)
+    bw = sfm.BlockWeights(mixed)
+    bw.c.down = sfm.qweight(sfm.SFM_W_FP8_E4M3, *fp8.down)           # FFN halves in different formats
+    with pytest.raises(sfm.SfmError, match="down: format"):
+        block_call(bw)
+    bw = sfm.BlockWeights(nf4)
+    bw.c.gate_up = sfm.qweight(sfm.SFM_W_MXFP4, *mixed.gate_up)       # MXFP4 FFN under NF4 attention
+    bw.c.down = sfm.qweight(sfm.SFM_W_MXFP4, *mixed.down)
+    with pytest.raises(sfm.SfmError, match="gate_up: format"):
+        block_call(bw)
+
+    import dataclasses
+    mp = synth.model_params(w.shape, w.layers, (0, w.name), device=DEV, fmt="mixed")
+    mp = dataclasses.replace(mp, blocks=[mp.blocks[0], fp8])           # layer 1 all FP8
+    text, z, t, _ = synth.step_inputs(w, device=DEV)
+    v = torch.empty(1, w.gh * w.gw, 128, device=DEV)
+    wsm = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw))
+    with pytest.raises(sfm.SfmError, match="FFN weight format of layer 0"):
+        sfm.sfm_model_velocity(ctx_tiny, sfm.ModelWeights(mp), text, z, t, v, 1, w.T, w.gh, w.gw, wsm)
+
+    p, e = synth.mxfp4_weight(256, 128, ("mx_args_k",), device=DEV)
+    a = torch.zeros(4, 128, dtype=torch.uint8, device=DEV)
+    sa = torch.ones(4, device=DEV)
+    out = torch.empty(4, 256, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(sfm.SfmError, match="k % 256"):
+        sfm.sfm_linear(ctx_tiny, 0, a, sa, sfm.qweight(sfm.SFM_W_MXFP4, p, e), out)
+    p, e = synth.mxfp4_weight(256, 256, ("mx_args_s",), device=DEV)
+    a = torch.zeros(4, 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(sfm.SfmError, match="a_scale"):
+        sfm.sfm_linear(ctx_tiny, 0, a, None, sfm.qweight(sfm.SFM_W_MXFP4, p, e), out)
+    p, e = synth.mxfp4_weight(8, 96, ("mx_args_d",), device=DEV)
+    with pytest.raises(sfm.SfmError, match="multiple of 64"):
+        sfm.sfm_dequant(ctx_tiny, sfm.qweight(sfm.SFM_W_MXFP4, p, e), torch.empty(8, 96, device=DEV))
+    torch.cuda.synchronize()
