@@ -273,3 +273,36 @@ def test_mxfp4_argument_checks(sfm, ctx_tiny):
     with pytest.raises(sfm.SfmError, match="multiple of 64"):
         sfm.sfm_dequant(ctx_tiny, sfm.qweight(sfm.SFM_W_MXFP4, p, e), torch.empty(8, 96, device=DEV))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,Nw,K,L", [(1, 256, 256, 1), (300, 256, 256, 150), (129, 512, 768, 129)])
+def test_linear_mxfp4_edge_shapes(sfm, ctx_tiny, M, Nw, K, L):
+    """The smallest weight (one 256 x 256 tile, two k stages), a single row,
+    three k stages, and the gated residual over two batches of a ragged M."""
+    _say("linear mxfp4 edge", M, Nw, K, L)
+    a = _rand_codes((M, K), ("lmxe", M, K))
+    sa = (torch.rand(M, generator=torch.Generator().manual_seed(5)) * 0.01 + 1e-3).float()
+    packed, ex = synth.mxfp4_weight(Nw, K, ("lmxew", Nw, K))
+    keep = (packed.to(DEV), ex.to(DEV))
+    w = sfm.qweight(sfm.SFM_W_MXFP4, *keep)
+    wd = N.mxfp4_dequant_f32(npu8(packed), npu8(ex), Nw, K).astype(np.float64)
+    y = (N.e4m3_decode(npu8(a)) @ wd.T) * sa.numpy()[:, None].astype(np.float64)
+    out = torch.empty(M, Nw, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_linear(ctx_tiny, 0, a.to(DEV), sa.to(DEV), w, out, M=M, L=L)
+    outs = torch.empty(M, Nw // 2, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_linear(ctx_tiny, 2, a.to(DEV), sa.to(DEV), w, outs, M=M, L=L)
+    Bn = (M + L - 1) // L
+    resid = synth.bf16_normal((M, Nw), ("lmxer", M), 1.0)
+    gate = synth.randn((Bn, Nw), ("lmxeg", M), 0.5)
+    outr = torch.empty(M, Nw, dtype=torch.bfloat16, device=DEV)
+    sfm.sfm_linear(ctx_tiny, 1, a.to(DEV), sa.to(DEV), w, outr, resid.to(DEV), gate.to(DEV), Nw, M=M, L=L)
+    torch.cuda.synchronize()
+    # both sides round nearly equal fp32 values to bf16 on their own, so single
+    # elements may sit one bf16 ulp (2^-8 relative) apart; over a few hundred
+    # outputs a handful of such ties already reaches 2e-3, so small outputs get
+    # the one-ulp bar
+    bar = 2e-3 if M * Nw >= 8192 else 4e-3
+    assert rel_l2(np64(out), N.bf16_round(y)) < bar
+    assert rel_l2(np64(outs), N.bf16_round(O.silu(y[:, :Nw // 2]) * y[:, Nw // 2:])) < bar
+    ref = N.bf16_round(np64(resid) + np64(gate)[np.arange(M) // L] * y)
+    assert rel_l2(np64(outr) - np64(resid), ref - np64(resid)) < 1e-2
