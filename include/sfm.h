@@ -298,7 +298,8 @@ int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, co
 
 /* Workspace bytes of sfm_model_velocity_streamed: a velocity-model workspace
  * plus two device slots for one block's FP8 weights each (~274 MB at the spec
- * dims). */
+ * dims); a slot also holds a mixed block (its MXFP4 FFN weights are smaller),
+ * of which only the block's own bytes are copied. */
 size_t sfm_streamed_workspace_bytes(const sfm_context* ctx, int B, int T, int gh, int gw);
 
 /* sfm_model_velocity with the blocks' weights in host memory (SimpleTuner
@@ -307,6 +308,7 @@ size_t sfm_streamed_workspace_bytes(const sfm_context* ctx, int B, int T, int gh
  * forward pass, trading speed for device memory).  Every pointer of
  * mw->blocks[i] points to host memory, pinned (hipHostMalloc) for the copies
  * to overlap the computation; the other weights of mw are device memory.
+ * Blocks may be FP8 or mixed (MXFP4 FFN), all layers alike.
  * Block i + 1's weights are copied into one of two workspace slots on a
  * context-owned copy stream while block i computes from the other; results
  * equal sfm_model_velocity's bitwise.  Calls on one context are serialised.
