@@ -2,6 +2,8 @@
 // mapping of a workgroup's weight-tile rows onto weight rows.
 #pragma once
 
+#include <atomic>
+#include <cstdint>
 #include <type_traits>
 
 #include "sfm_internal.h"
@@ -205,6 +207,18 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
 // XCD b % 8); renumber so that each XCD gets one contiguous range of ids and
 // the tiles it works on at the same time share its L2.
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per
+// device: the attribute is held per device, and `done` keeps one bit per device
+// ordinal (0..63) for the kernel it belongs to.
+inline void raise_lds_limit_once(const void* kern, size_t bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_acquire) & bit) return;
+    (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    done.fetch_or(bit, std::memory_order_release);
+}
+
 __device__ __forceinline__ int xcd_tile_id() {
     const int b = blockIdx.x, n = gridDim.x;
     const int q = n >> 3, r = n & 7, x = b & 7;

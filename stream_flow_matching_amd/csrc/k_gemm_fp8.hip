@@ -374,11 +374,8 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
     // two ring stages, then the epilogue's scales (row, column and three gate rows)
     const size_t shm = GemmLds<BM, BN, EPI, WF>::BYTES;
     auto kern = gemm_fp8_kernel<BM, BN, EPI, WF>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};
+    raise_lds_limit_once((const void*)kern, shm, lds_raised);
     hipLaunchKernelGGL(kern, dim3(ntm * ntn * splits), dim3(256), shm, st, a, sa, w, sw, wexp, out, resid, gate,
                        gate_stride, M, N, K, L, ntm, ntn, kps, part);
     return hipGetLastError();

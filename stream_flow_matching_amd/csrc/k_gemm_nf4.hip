@@ -262,11 +262,8 @@ hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, cons
     const int ntn = N / BN;
     const size_t shm = (size_t)2 * (BM + BN) * kRowB + 1024 + (size_t)(BM + 4 * BN) * 4;
     auto kern = gemm_nf4_kernel<BM, BN, EPI>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_raised{0};
+    raise_lds_limit_once((const void*)kern, shm, lds_raised);
     hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), shm, st, a, w, am, code, out, resid, gate, gate_stride, M, N,
                        K, L, ntm, ntn);
     return hipGetLastError();
