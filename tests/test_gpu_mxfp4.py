@@ -15,7 +15,7 @@ import torch
 from oracle import dit as O
 from oracle import numerics as N
 from stream_flow_matching_amd import synth
-from tests._util import np64, npu8, oracle_block, rel_l2, to_device
+from tests._util import np64, npu8, oracle_block, oracle_model, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -306,3 +306,28 @@ def test_linear_mxfp4_edge_shapes(sfm, ctx_tiny, M, Nw, K, L):
     assert rel_l2(np64(outs), N.bf16_round(O.silu(y[:, :Nw // 2]) * y[:, Nw // 2:])) < bar
     ref = N.bf16_round(np64(resid) + np64(gate)[np.arange(M) // L] * y)
     assert rel_l2(np64(outr) - np64(resid), ref - np64(resid)) < 1e-2
+
+
+def test_cfg_step_mixed_tiny_34_layers(sfm, ctx_tiny):
+    """34-layer cond + uncond models with mixed weights (FP8 attention
+    projections, MXFP4 FFN) at the tiny width: both velocities, the guided
+    velocity and the update against the oracle, within the 34-layer bar."""
+    _say("cfg step mixed tiny 34")
+    w = synth.Workload("tiny_step_mx", synth.TINY, 1, 16, 16, 16, layers=34)
+    cond = synth.model_params(w.shape, 34, (0, "tiny_cond_mx"), fmt="mixed")
+    unc = synth.model_params(w.shape, 34, (0, "tiny_uncond_mx"), fmt="mixed")
+    text, z, t, dt = synth.step_inputs(w)
+    cm, um = sfm.ModelWeights(to_device(cond)), sfm.ModelWeights(to_device(unc))
+    ws = sfm.workspace(sfm.sfm_step_workspace_bytes(ctx_tiny, 1, w.T, w.gh, w.gw))
+    vc = torch.empty(1, w.gh * w.gw, 128, device=DEV)
+    vu = torch.empty_like(vc)
+    zo = torch.empty_like(vc)
+    sfm.sfm_cfg_step(ctx_tiny, cm, um, text.to(DEV), z.to(DEV), zo, t, dt, 4.0, 1, w.T, w.gh, w.gw, ws, vc, vu)
+    torch.cuda.synchronize()
+    z2, v, rvc, rvu = O.cfg_step(np64(text), np64(z), [t], dt, 4.0, oracle_model(cond), oracle_model(unc), w.gh,
+                                 w.gw, O.TINY)
+    assert rel_l2(vc.cpu().numpy(), rvc) < 3e-2
+    assert rel_l2(vu.cpu().numpy(), rvu) < 3e-2
+    gv = vu.cpu().numpy().astype(np.float64) + 4.0 * (vc.cpu().numpy() - vu.cpu().numpy())
+    assert rel_l2(gv, v) < 3e-2
+    assert rel_l2(zo.cpu().numpy() - np64(z), z2 - np64(z)) < 3e-2
