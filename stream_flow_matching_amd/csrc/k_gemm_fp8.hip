@@ -267,6 +267,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int v = 0; v < NV; ++v) vmem(v, smem, ra, rb, kbeg);
 #pragma unroll
     for (int v = 0; v < NV; ++v) vmem(v, smem + STAGE, ra, rb, kbeg + kBK);
+    // the partial-sum pointer is only read by the epilogue: take it here, under the wait below,
+    // so that no scalar load is in flight when the loop starts (with one pending, the loop head
+    // would have to wait for every LDS read, as scalar loads return out of order)
+    if constexpr (EPI == kEpiPartial) asm volatile("" ::"s"(part));
     wait_vm_lgkm0<NV>();
 #pragma unroll
     for (int k = 0; k < NSL; ++k)
