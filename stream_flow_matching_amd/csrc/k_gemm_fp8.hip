@@ -386,23 +386,26 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
 }
 
 // Rounds of workgroups over the 256 compute units times the work of one tile,
-// divided by the main loop's measured efficiency at that tile shape.
-inline double tile_cost(int M, int N, int BM, int BN, double eff) {
+// divided by the main loop's measured efficiency at that tile shape.  With
+// `shared` (another pass's kernels fill the last round) the tiles count one by
+// one instead of in whole rounds.
+inline double tile_cost(int M, int N, int BM, int BN, double eff, bool shared) {
     const int64_t tiles = (int64_t)((M + BM - 1) / BM) * (N / BN);
-    return (double)((tiles + 255) / 256) * BM * BN / eff;
+    return (double)(shared ? tiles : (tiles + 255) / 256 * 256) * BM * BN / eff;
 }
 
 template <int EPI, int WF = 0>
 hipError_t launch_epi(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
-                      hipStream_t st, const uint8_t* wexp = nullptr) {
+                      hipStream_t st, const uint8_t* wexp = nullptr, bool shared = false) {
     // the cheapest of the tile shapes that divide N (256 x 192 for the gated residual only)
     double best = 1e300;
     int cfg = 3;
-    const double c256 = N % 256 == 0 ? tile_cost(M, N, 256, 256, 0.93) : 1e300;
-    const double c192 = EPI == SFM_EPI_RESID_GATE && N % 192 == 0 ? tile_cost(M, N, 256, 192, 0.92) : 1e300;
-    const double c128 = tile_cost(M, N, 256, 128, 0.81);
-    const double c64 = tile_cost(M, N, 128, 128, 0.70);
+    const double c256 = N % 256 == 0 ? tile_cost(M, N, 256, 256, 0.93, shared) : 1e300;
+    const double c192 =
+        EPI == SFM_EPI_RESID_GATE && N % 192 == 0 ? tile_cost(M, N, 256, 192, 0.92, shared) : 1e300;
+    const double c128 = tile_cost(M, N, 256, 128, 0.81, shared);
+    const double c64 = tile_cost(M, N, 128, 128, 0.70, shared);
     if (c256 < best) best = c256, cfg = 0;
     if (c192 < best) best = c192, cfg = 1;
     if (c128 < best) best = c128, cfg = 2;
@@ -452,15 +455,15 @@ hipError_t launch_gemm_fp8_splitk(const uint8_t* a, const float* sa, const uint8
 
 hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
-                           int K, int L, hipStream_t st) {
+                           int K, int L, hipStream_t st, bool shared) {
     if (M == 0) return hipSuccess;
     switch (epi) {
         case SFM_EPI_STORE:
-            return launch_epi<SFM_EPI_STORE>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+            return launch_epi<SFM_EPI_STORE>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, nullptr, shared);
         case SFM_EPI_RESID_GATE:
-            return launch_epi<SFM_EPI_RESID_GATE>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+            return launch_epi<SFM_EPI_RESID_GATE>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, nullptr, shared);
         case SFM_EPI_SWIGLU:
-            return launch_epi<SFM_EPI_SWIGLU>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st);
+            return launch_epi<SFM_EPI_SWIGLU>(a, sa, w, sw, out, resid, gate, gate_stride, M, N, K, L, st, nullptr, shared);
         default:
             return hipErrorInvalidValue;
     }
@@ -468,17 +471,18 @@ hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uin
 
 hipError_t launch_gemm_mx(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const uint8_t* wexp,
                           uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
-                          int K, int L, hipStream_t st) {
+                          int K, int L, hipStream_t st, bool shared) {
     if (M == 0) return hipSuccess;
     switch (epi) {
         case SFM_EPI_STORE:
-            return launch_epi<SFM_EPI_STORE, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st, wexp);
+            return launch_epi<SFM_EPI_STORE, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st,
+                                                wexp, shared);
         case SFM_EPI_RESID_GATE:
             return launch_epi<SFM_EPI_RESID_GATE, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st,
-                                                     wexp);
+                                                     wexp, shared);
         case SFM_EPI_SWIGLU:
             return launch_epi<SFM_EPI_SWIGLU, 1>(a, sa, w, nullptr, out, resid, gate, gate_stride, M, N, K, L, st,
-                                                 wexp);
+                                                 wexp, shared);
         default:
             return hipErrorInvalidValue;
     }

@@ -198,14 +198,17 @@ int check_block_weights(const sfm_dims* d, const sfm_block_weights* w, int* fmt_
     return SFM_OK;
 }
 
+// shared: another pass runs on the GPU at the same time (the FP8 / MXFP4 launchers then pick
+// tiles by efficiency alone)
 hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa, const sfm_qweight* w, uint16_t* out,
-                const uint16_t* resid, const float* gate, int64_t gs, int M, int L, hipStream_t st) {
+                const uint16_t* resid, const float* gate, int64_t gs, int M, int L, hipStream_t st,
+                bool shared = false) {
     if (w->fmt == SFM_W_FP8_E4M3)
         return launch_gemm_fp8(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, (const float*)w->scale, out, resid,
-                               gate, gs, M, w->n, w->k, L, st);
+                               gate, gs, M, w->n, w->k, L, st, shared);
     if (w->fmt == SFM_W_MXFP4)
         return launch_gemm_mx(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, (const uint8_t*)w->scale, out, resid,
-                              gate, gs, M, w->n, w->k, L, st);
+                              gate, gs, M, w->n, w->k, L, st, shared);
     Nf4Code code;
     memcpy(code.v, ctx->nf4_code, sizeof code.v);
     return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, (const float*)w->scale, code, out, resid,
@@ -244,7 +247,7 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
     SFM_LAUNCH(launch_gemv(c, 1, w->mod_w, w->mod_b, b.mod, B, 4 * D, d->adaln_dim, st));
     if (fmt == SFM_W_FP8_E4M3) {
         SFM_LAUNCH(launch_adaln_fp8(x_in, L, 0, L, b.mod, ms, b.hq, b.hs, B, D, d->eps, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st, shared));
     } else {
         SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, b.mod, ms, b.h, B, D, d->eps, st));
         SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
@@ -255,14 +258,15 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
     if (fmt == SFM_W_FP8_E4M3) {
         SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, b.mod + D, ms, M, L, st, shared));
         SFM_LAUNCH(launch_adaln_fp8(x_out, L, 0, L, b.mod + 2 * D, ms, b.hq, b.hs, B, D, d->eps, st));
         SFM_LAUNCH(mark(timed ? timer->begin : nullptr));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st, shared));
         SFM_LAUNCH(mark(timed ? timer->end : nullptr));
         if (timed) ++timer->used;
         SFM_LAUNCH(launch_quant_rows(s, M, F, b.oq, b.os, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
+        SFM_LAUNCH(
+            gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st, shared));
     } else {
         SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.o, nullptr, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
         SFM_LAUNCH(launch_adaln_bf16(x_out, L, 0, L, b.mod + 2 * D, ms, b.h, B, D, d->eps, st));

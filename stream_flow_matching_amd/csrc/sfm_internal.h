@@ -164,14 +164,16 @@ hipError_t launch_rmsnorm_f32_quant(const float* x, int rows, int cols, const ui
 hipError_t launch_timestep_embed(float t, float* e, int B, int dim, hipStream_t st);
 
 // k_gemm_fp8.hip
+// shared: another pass's kernels run on the GPU at the same time and fill the last round of
+// tiles, so the tile shape is chosen by main-loop efficiency alone (else by whole rounds too)
 hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const float* sw,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
-                           int K, int L, hipStream_t st);
+                           int K, int L, hipStream_t st, bool shared = false);
 // MXFP4 weights: w packed E2M1 nibbles [N][K/2] (element 2i in the low nibble), wexp E8M0
 // exponents [N][K/32]; FP8 activation codes as for launch_gemm_fp8; K % 256 == 0
 hipError_t launch_gemm_mx(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const uint8_t* wexp,
                           uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
-                          int K, int L, hipStream_t st);
+                          int K, int L, hipStream_t st, bool shared = false);
 // Split-K FP8 STORE projection for few rows and long K (few output tiles): splitk_parts(M, N, K)
 // parts of fp32 partial sums in `part` ([parts][M][N]), then a reduce applying sa, sw and the
 // bf16 rounding.  1 part means the plain launch would fill the chip as well.
