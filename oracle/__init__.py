@@ -39,16 +39,29 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
                          weights both formats hold exactly; per-block scales; the
                          mixed block equals the FP8 block on such weights
   silu, timestep_embedding   closed forms
+  modulation             (tests/test_oracle_block_pins.py) unit-vector weights: SiLU of
+                         c plus bias, chunk-major order (scale_a, gate_a, scale_m, gate_m)
+  timestep_mlp           identity-like weights against the closed form with SiLU
   rms_normalize, adaln_norm  invariants (unit RMS, scale invariance, scale -1 -> 0)
   quantize_rows_e4m3, fp8_linear  identity on representable rows, brute-force
                          matmul when quantisation is exact, zero rows, power-of-two
                          scaling, bounded quantisation error
   positions, mrope_*     layout written out, closed-form angles, pair norms,
                          identity at position 0, relative-position property,
-                         one axis moves one section
+                         one axis moves one section; a unit pair turns to
+                         (cos, sin) (RoFormer's rotation direction)
+  qk_norm_rope           +-1 rows with power-of-two gamma give +-gamma; a random row
+                         with gamma != 1 against a hand loop
+  nf4_linear             brute force with torch's fp32 product and bf16 cast of the
+                         dequantised weight
   attention              brute force on tiny sequences, special cases
   block_forward          gate 0 and scale -1 identities, row-subset and batch
-                         consistency
+                         consistency; each branch switched off by its own chunk
+                         (gate_a = 0 with scale_m = -1 and the converse); an
+                         MLP-only update computed by hand (SwiGLU operand order,
+                         scale_m / gate_m wiring); attention half then MLP half
+                         equals the block (the MLP reads x1); value rows and the
+                         output projection's orientation by hand
   model_velocity         zero-layer reduction to the final layer of the embedding
   euler_cfg, cfg_step    closed forms; uncond ignores text; guidance 1 gives cond
   param_count            the ~9.3B of the spec table
@@ -59,9 +72,10 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
   sampler presets        the research note's preset table (tests/golden)
   sampler.euler_loop / sample   constant velocity telescopes to z + v, the linear
                          ODE's product form, chaining of the guided steps
-Parity unpinned: the whole model against a real checkpoint (none exists here);
-the modulation chunk order, the timestep MLP and the final layer are readings
-of prose, pinned only structurally.
+Parity unpinned: the whole model against a real checkpoint (none exists here).
+The modulation chunk order, the timestep MLP and the final layer are readings
+of prose: the pins fix that the oracle computes exactly those readings, not
+that a trained Ideogram 4 uses them.
 """
 
 from . import numerics, dit, sampler  # noqa: F401

@@ -388,7 +388,11 @@ def test_model_velocity_zero_layers_reduces_to_final_layer_of_embedding():
     # with no blocks the text prefix cannot reach the image tokens
     assert np.array_equal(v, v_u)
     # textbook composition of the three linear maps, written with explicit loops for one token
-    c = O.timestep_mlp([0.3], mw)[0]
+    # timestep MLP written out: sinusoidal embedding, Linear, SiLU, Linear
+    f = [10000.0 ** (-i / 256.0) for i in range(256)]
+    e = np.array([math.cos(300.0 * fi) for fi in f] + [math.sin(300.0 * fi) for fi in f])
+    hdn = np.asarray(mw.t_w1, np.float64) @ e + mw.t_b1
+    c = np.asarray(mw.t_w2, np.float64) @ np.array([v / (1.0 + math.exp(-v)) for v in hdn]) + mw.t_b2
     xi = N.bf16_round(z[0, 4] @ np.asarray(mw.x_w).T + mw.x_b)
     sf = O.silu(c) @ np.asarray(mw.f_mod_w).T
     r = math.sqrt(sum(t * t for t in xi) / 512 + 1e-6)
