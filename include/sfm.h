@@ -129,8 +129,9 @@ typedef struct sfm_block_weights {
     const float* mod_b;
 } sfm_block_weights;
 
-/* Velocity-model weights.  blocks: host array of num_layers block weights
- * (FP8).  x_w bf16 [D][C], x_b fp32 [D]: latent-to-token embedding.  t_w1,
+/* Velocity-model weights.  blocks: host array of num_layers block weights,
+ * FP8 or mixed (FP8 attention projections, MXFP4 FFN; every layer with the
+ * FFN format of layer 0).  x_w bf16 [D][C], x_b fp32 [D]: latent-to-token embedding.  t_w1,
  * t_w2 bf16 [A][A], t_b1, t_b2 fp32 [A]: timestep MLP.  f_mod_w bf16 [D][A],
  * f_mod_b fp32 [D]: final-layer AdaLN scale.  f_w bf16 [C][D], f_b fp32 [C]:
  * projection back to latent channels. */
@@ -189,7 +190,8 @@ typedef enum sfm_epilogue {
  * matrix cores, the NF4 decode fused into the weight-operand load.
  * gate: fp32, row b of the batch at gate + b*gate_batch_stride (n values);
  * L gives the batch of a row (b = m / L); with the gated residual and rows in
- * more than one batch (M > L), L >= 128.  k % 256 == 0, n % 256 == 0. */
+ * more than one batch (M > L), L >= 128.  k % 256 == 0, n % 256 == 0 and
+ * n * k < 2^31 (SFM_E_SHAPE otherwise); M is limited only by int range. */
 int sfm_linear(const sfm_context* ctx, int epilogue, const void* a, const float* a_scale, const sfm_qweight* w,
                uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_batch_stride, int M, int L,
                void* stream);
@@ -349,7 +351,7 @@ int sfm_cfg_step_varlen(const sfm_context* ctx, const sfm_model_weights* cond, c
                         float guidance, int B, int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws,
                         size_t ws_bytes, void* stream);
 
-/* ---------------------------------------------------------------- text conditioning *//* ---------------------------------------------------------------- text conditioning */
+/* ---------------------------------------------------------------- text conditioning */
 
 /* Workspace bytes of sfm_text_project for M tokens of k_raw features (with
  * room for the fp32 partial sums of a split-K projection when M is small). */
@@ -372,7 +374,7 @@ size_t sfm_text_project_workspace_bytes(const sfm_context* ctx, int M, int k_raw
 int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
                      uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream);
 
-/* ---------------------------------------------------------------- sampler *//* ---------------------------------------------------------------- sampler */
+/* ---------------------------------------------------------------- sampler */
 
 /* Time grid of the logit-normal schedule (research note, "Training method":
  * logit-normal noise schedule with parameters (mu, std), mu shifted by

@@ -204,9 +204,6 @@ __device__ __forceinline__ void gemm_epilogue_lds(const v16f (&acc)[FM][FN], uin
     }
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
-// XCD b % 8); renumber so that each XCD gets one contiguous range of ids and
-// the tiles it works on at the same time share its L2.
 // Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per
 // device: the attribute is held per device, and `done` keeps one bit per device
 // ordinal (0..63) for the kernel it belongs to.
@@ -219,6 +216,9 @@ inline void raise_lds_limit_once(const void* kern, size_t bytes, std::atomic<uin
     done.fetch_or(bit, std::memory_order_release);
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8); renumber so that each XCD gets one contiguous range of ids and
+// the tiles it works on at the same time share its L2.
 __device__ __forceinline__ int xcd_tile_id() {
     const int b = blockIdx.x, n = gridDim.x;
     const int q = n >> 3, r = n & 7, x = b & 7;

@@ -23,9 +23,12 @@
 // max), which skips most rescales of the 128-register accumulator.
 //
 // The P V product runs in fp16 (P and V^T in fp16, fp32 accumulation): fp16
-// keeps 3 more mantissa bits of P than bf16, and V's bf16 values are exact in
-// fp16.  P in bf16 perturbs o by about 1e-3 relative, which the per-token FP8
-// quantisation of o downstream turns into percent-level changes of the block.
+// keeps 3 more mantissa bits of P than bf16.  V's bf16 values are exact in
+// fp16 from 2^-17 up to 65504; smaller magnitudes keep fp16's subnormal
+// quantum 2^-24 (an absolute error below 2^-25) and larger ones saturate to
+// +-65504 in the rotary kernel.  P in bf16 perturbs o by about 1e-3 relative,
+// which the per-token FP8 quantisation of o downstream turns into
+// percent-level changes of the block.
 //
 // Schedule: the work is the list of items (batch, head, block of 128 queries),
 // batch-major, each with its walk of key tiles.  The grid is one persistent

@@ -132,17 +132,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // wave-load v of this wave covers tile rows 8 (wave + 4 v) + (lane >> 3); the lane writes
     // physical chunk lane & 7, which holds logical chunk (lane & 7) ^ ((row >> 1) & 7), and
     // (row >> 1) & 7 == (4 (wave & 1) + (lane >> 4)) & 7 for every v
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0x7FFFFFFF, kRsrcWord3);
+    // The activation view starts at the tile's first row (64-bit base), so the 32-bit offsets
+    // stay below BM * K bytes whatever M * K is; the weight view (N * K < 2^31 bytes, checked
+    // by the host) starts at W.
+    const uint8_t* const A0 = A + (int64_t)m0 * K;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, 0x7FFFFFFF, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, 0x7FFFFFFF, kRsrcWord3);
     // zero-length views: loads through them touch no memory (the tail stages)
-    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, 0, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, 0, kRsrcWord3);
     const int lrow = lane >> 3, lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     uint32_t voff[NV];
 #pragma unroll
     for (int v = 0; v < AI; ++v) {
         const int row = min(m0 + 8 * (wave + 4 * v) + lrow, M - 1);
-        voff[v] = (uint32_t)row * (uint32_t)K + lch * 16;
+        voff[v] = (uint32_t)(row - m0) * (uint32_t)K + lch * 16;
     }
 #pragma unroll
     for (int v = 0; v < BI; ++v) {

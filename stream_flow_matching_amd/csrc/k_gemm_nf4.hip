@@ -117,14 +117,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // activation tile: wave-load v covers tile rows 8 (wave + 4 v) + (lane >> 3), physical chunk
     // lane & 7 holding logical chunk (lane & 7) ^ ((row >> 1) & 7)
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0x7FFFFFFF, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0, kRsrcWord3);
+    // the view starts at the tile's first row (64-bit base): 32-bit offsets stay below BM * 2K
+    // bytes whatever M * K is
+    const uint16_t* const A0 = A + (int64_t)m0 * K;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, 0x7FFFFFFF, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, 0, kRsrcWord3);
     const int lrow = lane >> 3, lch = (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
     uint32_t voff[AI];
 #pragma unroll
     for (int v = 0; v < AI; ++v) {
         const int row = min(m0 + 8 * (wave + 4 * v) + lrow, M - 1);
-        voff[v] = (uint32_t)row * (uint32_t)(K * 2) + lch * 16;
+        voff[v] = (uint32_t)(row - m0) * (uint32_t)(K * 2) + lch * 16;
     }
 
     // weight decode ownership: tile row br, elements eo .. eo + EPT - 1 of each stage

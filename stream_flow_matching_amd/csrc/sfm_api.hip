@@ -667,6 +667,9 @@ int sfm_linear(const sfm_context* ctx, int epi, const void* a, const float* a_sc
     SFM_CHECK(check_qweight(w, w->fmt, w->n, w->k, "w"));
     if (w->n < 256 || w->n % 256 || w->k < 256 || w->k % 256)
         return fail(SFM_E_SHAPE, "weight [%d][%d]: need n %% 256 == 0 and k %% 256 == 0", w->n, w->k);
+    // the kernels address the weight with 32-bit offsets from its base
+    if ((int64_t)w->n * w->k >= (int64_t)1 << 31)
+        return fail(SFM_E_SHAPE, "weight [%d][%d]: n * k must stay below 2^31", w->n, w->k);
     SFM_CHECK(check_ptr(a, "a"));
     SFM_CHECK(check_ptr(out, "out"));
     if (w->fmt != SFM_W_NF4_B64 && !a_scale) return fail(SFM_E_INVALID_ARG, "a_scale is NULL");
@@ -692,8 +695,9 @@ size_t sfm_text_project_workspace_bytes(const sfm_context* ctx, int M, int k_raw
     return c.off + 256;
 }
 
-int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
-                     uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int text_project_checks(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
+                        uint16_t* text_out, int M) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     if (!proj) return fail(SFM_E_INVALID_ARG, "proj is NULL");
     const int D = ctx->dims.emb_dim, K = proj->k;
@@ -703,17 +707,20 @@ int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* n
     SFM_CHECK(check_ptr(raw, "raw"));
     SFM_CHECK(check_ptr(norm_w, "norm_w"));
     SFM_CHECK(check_ptr(text_out, "text_out"));
-    SFM_CHECK(check_ptr(ws, "ws"));
     if (M < 0) return fail(SFM_E_SHAPE, "M < 0");
-    const size_t need = sfm_text_project_workspace_bytes(ctx, M, K);
-    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return SFM_OK;
+}
+
+// Enqueue the projection with its codes, scales and partial sums carved from ws (checked).
+int text_project_run(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
+                     uint16_t* text_out, int M, void* ws, hipStream_t st) {
+    const int D = ctx->dims.emb_dim, K = proj->k;
     if (M == 0) return SFM_OK;
     Carve c(ws);
     uint8_t* codes = c.take<uint8_t>((size_t)M * K);
     float* scales = c.take<float>((size_t)M);
     const int parts = splitk_parts(M, D, K);
     float* part = parts > 1 ? c.take<float>((size_t)parts * M * D) : nullptr;
-    const hipStream_t st = (hipStream_t)stream;
     SFM_LAUNCH(launch_rmsnorm_f32_quant(raw, M, K, norm_w, codes, scales, ctx->dims.eps, st));
     // a prompt has few rows and the features are long: split K when the output tiles alone would
     // leave most of the compute units idle
@@ -724,6 +731,16 @@ int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* n
         SFM_LAUNCH(launch_gemm_fp8(SFM_EPI_STORE, codes, scales, (const uint8_t*)proj->q, (const float*)proj->scale,
                                    text_out, nullptr, nullptr, 0, M, D, K, M, st));
     return SFM_OK;
+}
+}  // namespace
+
+int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
+                     uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream) {
+    SFM_CHECK(text_project_checks(ctx, raw, norm_w, proj, text_out, M));
+    SFM_CHECK(check_ptr(ws, "ws"));
+    const size_t need = sfm_text_project_workspace_bytes(ctx, M, proj->k);
+    if (ws_bytes < need) return fail(SFM_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return text_project_run(ctx, raw, norm_w, proj, text_out, M, ws, (hipStream_t)stream);
 }
 
 int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,

@@ -252,11 +252,19 @@ class ModelParams:
     f_b: torch.Tensor
 
 
-def model_params(shape: Shape, layers, key, device="cpu", fmt="fp8") -> ModelParams:
-    """fmt: the blocks' weight format, "fp8" or "mixed"."""
+def model_params(shape: Shape, layers, key, device="cpu", fmt="fp8", workers=1) -> ModelParams:
+    """fmt: the blocks' weight format, "fp8" or "mixed".  workers > 1 draws the
+    blocks in a thread pool (each tensor has its own generator, so the bytes
+    are the same as with one worker)."""
     D, A, C = shape.emb_dim, shape.adaln_dim, shape.latent_ch
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            blocks = list(ex.map(lambda i: block_params(shape, key + ("layer", i), fmt, device), range(layers)))
+    else:
+        blocks = [block_params(shape, key + ("layer", i), fmt, device) for i in range(layers)]
     return ModelParams(
-        blocks=[block_params(shape, key + ("layer", i), fmt, device) for i in range(layers)],
+        blocks=blocks,
         x_w=bf16_normal((D, C), key + ("x_w",), C ** -0.5, device=device),
         x_b=randn((D,), key + ("x_b",), 0.02, device),
         t_w1=bf16_normal((A, A), key + ("t_w1",), A ** -0.5, device=device),

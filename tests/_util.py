@@ -70,3 +70,19 @@ def vt_order(n):
             for e in range(8):
                 idx[j + 8 * g + e] = j + 4 * g + (e if e < 4 else 12 + e)
     return idx
+
+
+def check_rel(tag, got, ref, bar) -> float:
+    """rel-L2 of got against ref, reported with its bar (stderr, and one JSON line
+    appended to the file named by SFM_MARGINS when set), then asserted < bar."""
+    import json
+    import os
+    import sys
+    err = rel_l2(got, ref)
+    print(f"[margin] {tag}: rel-L2 {err:.3e} (bar {bar:.1e})", file=sys.stderr, flush=True)
+    path = os.environ.get("SFM_MARGINS")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": tag, "rel_l2": err, "bar": bar}) + "\n")
+    assert err < bar, f"{tag}: rel-L2 {err:.3e} >= {bar}"
+    return err

@@ -15,7 +15,7 @@ import torch
 from oracle import dit as O
 from oracle import numerics as N
 from stream_flow_matching_amd import synth
-from tests._util import np64, npu8, oracle_block, oracle_model, rel_l2, to_device
+from tests._util import check_rel, np64, npu8, oracle_block, oracle_model, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -103,9 +103,9 @@ def test_linear_mxfp4(sfm, ctx_tiny, epi, M):
             ref = N.bf16_round(np64(resid) + np64(gate)[np.arange(M) // L] * y)
     torch.cuda.synchronize()
     got = np64(out)
-    assert rel_l2(got, ref) < 2e-3
+    check_rel("test_linear_mxfp4#1", got, ref, 2e-3)
     if epi == 1:
-        assert rel_l2(got - np64(resid), ref - np64(resid)) < 1e-2
+        check_rel("test_linear_mxfp4#2", got - np64(resid), ref - np64(resid), 1e-2)
 
 
 def test_linear_mxfp4_full_width_sampled(sfm, ctx_full):
@@ -125,7 +125,7 @@ def test_linear_mxfp4_full_width_sampled(sfm, ctx_full):
     wd = N.mxfp4_dequant_f32(npu8(packed), npu8(ex), 2 * F, D).astype(np.float64)
     y = (N.e4m3_decode(npu8(a[rows])) @ wd.T) * sa.numpy()[rows, None].astype(np.float64)
     ref = N.bf16_round(O.silu(y[:, :F]) * y[:, F:])
-    assert rel_l2(np64(out[rows]), ref) < 2e-3
+    check_rel("test_linear_mxfp4_full_width_sampled#1", np64(out[rows]), ref, 2e-3)
     del keep, w, out, wd
     # down projection: K 12288, gated residual in place, three batches of L 1536
     a2 = _rand_codes((M, F), ("lmxf2",))
@@ -142,8 +142,8 @@ def test_linear_mxfp4_full_width_sampled(sfm, ctx_full):
     y2 = (N.e4m3_decode(npu8(a2[rows])) @ wd2.T) * sa.numpy()[rows, None].astype(np.float64)
     ref2 = N.bf16_round(np64(resid[rows]) + np64(gate)[rows // L] * y2)
     got2 = np64(x[rows])
-    assert rel_l2(got2, ref2) < 2e-3
-    assert rel_l2(got2 - np64(resid[rows]), ref2 - np64(resid[rows])) < 1e-2
+    check_rel("test_linear_mxfp4_full_width_sampled#2", got2, ref2, 2e-3)
+    check_rel("test_linear_mxfp4_full_width_sampled#3", got2 - np64(resid[rows]), ref2 - np64(resid[rows]), 1e-2)
 
 
 def _run_block(sfm, ctx, w, p, x, c):
@@ -164,8 +164,8 @@ def test_block_mixed_tiny(sfm, ctx_tiny):
     xo = _run_block(sfm, ctx_tiny, w, p, x, c)
     ref = O.block_forward(np64(x), c.numpy().astype(np.float64), oracle_block(p), w.T, w.gh, w.gw, O.TINY)
     got = np64(xo)
-    assert rel_l2(got, ref) < 1e-2
-    assert rel_l2(got - np64(x), ref - np64(x)) < UPDATE_BAR
+    check_rel("test_block_mixed_tiny#1", got, ref, 1e-2)
+    check_rel("test_block_mixed_tiny#2", got - np64(x), ref - np64(x), UPDATE_BAR)
 
 
 def test_block_mixed_full_sampled(sfm, ctx_full):
@@ -181,8 +181,8 @@ def test_block_mixed_full_sampled(sfm, ctx_full):
                           rows=rows)
     got = np64(xo).reshape(M, -1)[rows]
     xin = np64(x).reshape(M, -1)[rows]
-    assert rel_l2(got, ref) < 1e-2
-    assert rel_l2(got - xin, ref - xin) < UPDATE_BAR
+    check_rel("test_block_mixed_full_sampled#1", got, ref, 1e-2)
+    check_rel("test_block_mixed_full_sampled#2", got - xin, ref - xin, UPDATE_BAR)
 
 
 def _pinned(obj):
@@ -302,10 +302,10 @@ def test_linear_mxfp4_edge_shapes(sfm, ctx_tiny, M, Nw, K, L):
     # outputs a handful of such ties already reaches 2e-3, so small outputs get
     # the one-ulp bar
     bar = 2e-3 if M * Nw >= 8192 else 4e-3
-    assert rel_l2(np64(out), N.bf16_round(y)) < bar
-    assert rel_l2(np64(outs), N.bf16_round(O.silu(y[:, :Nw // 2]) * y[:, Nw // 2:])) < bar
+    check_rel("test_linear_mxfp4_edge_shapes#1", np64(out), N.bf16_round(y), bar)
+    check_rel("test_linear_mxfp4_edge_shapes#2", np64(outs), N.bf16_round(O.silu(y[:, :Nw // 2]) * y[:, Nw // 2:]), bar)
     ref = N.bf16_round(np64(resid) + np64(gate)[np.arange(M) // L] * y)
-    assert rel_l2(np64(outr) - np64(resid), ref - np64(resid)) < 1e-2
+    check_rel("test_linear_mxfp4_edge_shapes#3", np64(outr) - np64(resid), ref - np64(resid), 1e-2)
 
 
 def test_cfg_step_mixed_tiny_34_layers(sfm, ctx_tiny):
@@ -326,8 +326,8 @@ def test_cfg_step_mixed_tiny_34_layers(sfm, ctx_tiny):
     torch.cuda.synchronize()
     z2, v, rvc, rvu = O.cfg_step(np64(text), np64(z), [t], dt, 4.0, oracle_model(cond), oracle_model(unc), w.gh,
                                  w.gw, O.TINY)
-    assert rel_l2(vc.cpu().numpy(), rvc) < 3e-2
-    assert rel_l2(vu.cpu().numpy(), rvu) < 3e-2
+    check_rel("test_cfg_step_mixed_tiny_34_layers#1", vc.cpu().numpy(), rvc, 3e-2)
+    check_rel("test_cfg_step_mixed_tiny_34_layers#2", vu.cpu().numpy(), rvu, 3e-2)
     gv = vu.cpu().numpy().astype(np.float64) + 4.0 * (vc.cpu().numpy() - vu.cpu().numpy())
-    assert rel_l2(gv, v) < 3e-2
-    assert rel_l2(zo.cpu().numpy() - np64(z), z2 - np64(z)) < 3e-2
+    check_rel("test_cfg_step_mixed_tiny_34_layers#3", gv, v, 3e-2)
+    check_rel("test_cfg_step_mixed_tiny_34_layers#4", zo.cpu().numpy() - np64(z), z2 - np64(z), 3e-2)
