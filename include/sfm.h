@@ -374,6 +374,23 @@ size_t sfm_text_project_workspace_bytes(const sfm_context* ctx, int M, int k_raw
 int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
                      uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream);
 
+/* sfm_text_project for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The E4M3 codes, row scales and split-K partial sums live in a fixed device
+ * scratch of 128 MiB that the library holds on each GPU it runs on until the
+ * process ends; its device address is looked up once per device when a
+ * context is created.  Accepts every (M, k) whose
+ * sfm_text_project_workspace_bytes is at most 128 MiB (any prompt of up to
+ * 2048 tokens at 53,248 features); larger: SFM_E_WORKSPACE before any enqueue.
+ * Allocates nothing and calls no allocating routine.  The scratch keeps the
+ * last call's contents and every call on one GPU uses it: calls that overlap
+ * in time on one GPU (different streams or threads) race and give undefined
+ * results, so order them on one stream.  Results equal sfm_text_project's
+ * bitwise (the same kernels).  Errors as sfm_text_project, plus SFM_E_DEVICE
+ * when the context holds no scratch address. */
+int sfm_text_project_noalloc(const sfm_context* ctx, const float* raw, const uint16_t* norm_w,
+                             const sfm_qweight* proj, uint16_t* text_out, int M, void* stream);
+
 /* ---------------------------------------------------------------- sampler */
 
 /* Time grid of the logit-normal schedule (research note, "Training method":

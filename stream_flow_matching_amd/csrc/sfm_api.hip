@@ -18,6 +18,35 @@ namespace {
 thread_local std::string g_err;
 }  // namespace
 
+// Fixed device scratch of sfm_text_project_noalloc (for callers that cannot
+// allocate).  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses this name as an address: the device address is
+// taken once per device with hipGetSymbolAddress (scratch_address) and passed
+// on from there.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_lock;
+void* g_scratch_ptr[64] = {};  // per device ordinal
+
+// Device address of `scratch` on the current device `dev`, looked up on the first call for
+// that device (which must be current).
+hipError_t scratch_address(int dev, void** out) {
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
 int sfm::fail(int code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -579,6 +608,7 @@ int sfm_context_create(const sfm_dims* dims, int device, sfm_context** out) {
         if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->consumed[i], hipEventDisableTiming);
     }
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming);
+    if (e == hipSuccess) e = scratch_address(device, &ctx->scratch);
     (void)hipSetDevice(prev);
     if (e != hipSuccess) {
         sfm_context_destroy(ctx);
@@ -733,6 +763,17 @@ int text_project_run(const sfm_context* ctx, const float* raw, const uint16_t* n
     return SFM_OK;
 }
 }  // namespace
+
+int sfm_text_project_noalloc(const sfm_context* ctx, const float* raw, const uint16_t* norm_w,
+                             const sfm_qweight* proj, uint16_t* text_out, int M, void* stream) {
+    SFM_CHECK(text_project_checks(ctx, raw, norm_w, proj, text_out, M));
+    const size_t need = sfm_text_project_workspace_bytes(ctx, M, proj->k);
+    if (need > kScratchBytes)
+        return fail(SFM_E_WORKSPACE, "%d rows of %d features need %zu bytes of scratch, above the fixed %zu", M,
+                    proj->k, need, kScratchBytes);
+    if (!ctx->scratch) return fail(SFM_E_DEVICE, "no scratch address for device %d", ctx->device);
+    return text_project_run(ctx, raw, norm_w, proj, text_out, M, ctx->scratch, (hipStream_t)stream);
+}
 
 int sfm_text_project(const sfm_context* ctx, const float* raw, const uint16_t* norm_w, const sfm_qweight* proj,
                      uint16_t* text_out, int M, void* ws, size_t ws_bytes, void* stream) {

@@ -18,6 +18,7 @@ struct sfm_context {
     float nf4_code[16];   // NF4 codebook (fp32), passed to kernels by value
     int attn_grid = 0;    // attention workgroups: the device's compute units, at most 256
     float* attn_part = nullptr;  // partial results of the standalone attention calls
+    void* scratch = nullptr;     // device address of the library's static scratch on `device`
     // the two passes of a CFG step run on these streams at once (default priority);
     // the fork / join events order them against the caller's stream, and the lock
     // keeps concurrent steps on one context from interleaving their use of them

@@ -117,6 +117,7 @@ SIGNATURES = {
                                _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "sfm_text_project_workspace_bytes": (_SZ, [_P, _I, _I]),
     "sfm_text_project": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _I, _P, _SZ, _P]),
+    "sfm_text_project_noalloc": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _I, _P]),
     "sfm_time_grid": (_I, [_I, ctypes.c_double, ctypes.c_double, _I64, _P]),
     "sfm_preset": (_I, [_I, ctypes.POINTER(sfm_preset_info)]),
     "sfm_preset_schedule": (_I, [_I, _I, _I, _P, _P, _I]),
@@ -372,6 +373,13 @@ def sfm_text_project(ctx, raw, norm_w, proj, text_out, ws=None, stream=None):
         ws = workspace(lib().sfm_text_project_workspace_bytes(ctx.handle, M, raw.shape[-1]), raw.device)
     _check(lib().sfm_text_project(ctx.handle, _ptr(raw), _ptr(norm_w), ctypes.byref(proj), _ptr(text_out), M,
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sfm_text_project_noalloc(ctx, raw, norm_w, proj, text_out, stream=None):
+    """sfm_text_project on the library's fixed device scratch (no workspace argument)."""
+    M = raw.numel() // raw.shape[-1]
+    _check(lib().sfm_text_project_noalloc(ctx.handle, _ptr(raw), _ptr(norm_w), ctypes.byref(proj), _ptr(text_out), M,
+                                          _stream(stream)))
 
 
 def sfm_time_grid(n_steps, mu, std_dev, num_pixels):
