@@ -106,17 +106,18 @@ def quantize_rows_e4m3(a_bf16):
     return codes, alpha.astype(np.float64)
 
 
-def fp8_linear(a_bf16, w_codes, w_scale):
+def fp8_linear(a_bf16, w_codes, w_scale, w_decoded=None):
     """y[m, n] = (sum_k dec(Aq[m, k]) * dec(Wq[n, k])) * (alpha[m] / 448) * s_w[n].
 
     The weight is FP8-E4M3 with a per-output-channel fp32 scale ([Deploy]
     section 2: the original release is FP8 E4M3).  The activation is bf16 and
     is quantised per token to E4M3 (``quantize_rows_e4m3``) so that the product
     runs on FP8 x FP8 matrix units.  The float64 sum of products of two E4M3
-    values is exact at these sizes.  No bias.  Returns float64 [M, N].
+    values is exact at these sizes.  No bias.  w_decoded, when given, holds
+    e4m3_decode(w_codes) already (see ``predecode``).  Returns float64 [M, N].
     """
     codes, alpha = quantize_rows_e4m3(a_bf16)
-    acc = e4m3_decode(codes) @ e4m3_decode(w_codes).T
+    acc = e4m3_decode(codes) @ (e4m3_decode(w_codes) if w_decoded is None else w_decoded).T
     sa = alpha / E4M3_MAX
     return acc * sa[:, None] * np.asarray(w_scale, np.float64)[None, :]
 
@@ -143,9 +144,10 @@ def text_projection(raw, norm_w_bf16, proj_codes, proj_scale, eps=1e-6):
     return bf16_round(fp8_linear(h, proj_codes, proj_scale))
 
 
-def nf4_linear(a_bf16, packed, absmax, n, k):
-    """y = a @ bf16(W_nf4)^T: NF4 weights dequantised to bf16 operands, bf16 input."""
-    w = bf16_round(nf4_dequant_f32(packed, absmax, n, k).astype(np.float64))
+def nf4_linear(a_bf16, packed, absmax, n, k, w_decoded=None):
+    """y = a @ bf16(W_nf4)^T: NF4 weights dequantised to bf16 operands, bf16 input.
+    w_decoded, when given, holds that bf16 operand already (see ``predecode``)."""
+    w = bf16_round(nf4_dequant_f32(packed, absmax, n, k).astype(np.float64)) if w_decoded is None else w_decoded
     return np.asarray(a_bf16, np.float64) @ w.T
 
 
@@ -246,6 +248,7 @@ def attention(q, k, v, rows=None, chunk=512):
 class Fp8Weight:
     codes: np.ndarray   # uint8 [N, K]
     scale: np.ndarray   # float32 [N]
+    decoded: np.ndarray = None   # optional e4m3_decode(codes), float64 [N, K]
 
 
 @dataclass
@@ -254,6 +257,7 @@ class Nf4Weight:
     absmax: np.ndarray  # float32 [N*K/64]
     n: int
     k: int
+    decoded: np.ndarray = None   # optional bf16 operand values, float64 [N, K]
 
 
 @dataclass
@@ -262,9 +266,10 @@ class Mxfp4Weight:
     scales: np.ndarray  # uint8 E8M0 exponents [N, K/32]
     n: int
     k: int
+    decoded: np.ndarray = None   # optional weight values, float64 [N, K]
 
 
-def mxfp4_linear(a_bf16, packed, scales, n, k):
+def mxfp4_linear(a_bf16, packed, scales, n, k, w_decoded=None):
     """y[m, n] = (sum_k dec(Aq[m, k]) * w[n, k]) * (alpha[m] / 448), w = e2m1 * 2**(e - 127).
 
     [Deploy] section 2.2: in the mixed scheme the FFN linears hold 4-bit float
@@ -274,27 +279,48 @@ def mxfp4_linear(a_bf16, packed, scales, n, k):
     sum of products is exact.  No per-channel scale, no bias.
     """
     codes, alpha = quantize_rows_e4m3(a_bf16)
-    acc = e4m3_decode(codes) @ mxfp4_dequant_f32(packed, scales, n, k).astype(np.float64).T
+    wv = mxfp4_dequant_f32(packed, scales, n, k).astype(np.float64) if w_decoded is None else w_decoded
+    acc = e4m3_decode(codes) @ wv.T
     return acc * (alpha / E4M3_MAX)[:, None]
 
 
 def linear(a_bf16, w):
     if isinstance(w, Fp8Weight):
-        return fp8_linear(a_bf16, w.codes, w.scale)
+        return fp8_linear(a_bf16, w.codes, w.scale, w.decoded)
     if isinstance(w, Mxfp4Weight):
-        return mxfp4_linear(a_bf16, w.packed, w.scales, w.n, w.k)
-    return nf4_linear(a_bf16, w.packed, w.absmax, w.n, w.k)
+        return mxfp4_linear(a_bf16, w.packed, w.scales, w.n, w.k, w.decoded)
+    return nf4_linear(a_bf16, w.packed, w.absmax, w.n, w.k, w.decoded)
+
+
+def decoded_values(w):
+    """The values ``linear`` multiplies by: dec(codes) for FP8 (the per-channel
+    scale is applied after the sum), the weights for MXFP4, the bf16 operand
+    for NF4.  float64 [N, K]."""
+    if isinstance(w, Fp8Weight):
+        return e4m3_decode(w.codes)
+    if isinstance(w, Mxfp4Weight):
+        return mxfp4_dequant_f32(w.packed, w.scales, w.n, w.k).astype(np.float64)
+    return bf16_round(nf4_dequant_f32(w.packed, w.absmax, w.n, w.k).astype(np.float64))
+
+
+def predecode(bw):
+    """The block with every projection's decoded values attached (the products
+    then skip the decoding; the arithmetic is unchanged)."""
+    from dataclasses import replace
+    return replace(bw, **{name: replace(getattr(bw, name), decoded=decoded_values(getattr(bw, name)))
+                          for name in ("qkv", "o", "gate_up", "down")})
 
 
 def row_slice(w, r0, r1):
     """Output rows [r0, r1) of a quantised weight (for the q / k / v and gate / up parts)."""
+    dec = None if w.decoded is None else w.decoded[r0:r1]
     if isinstance(w, Fp8Weight):
-        return Fp8Weight(w.codes[r0:r1], w.scale[r0:r1])
+        return Fp8Weight(w.codes[r0:r1], w.scale[r0:r1], dec)
     if isinstance(w, Mxfp4Weight):
-        return Mxfp4Weight(w.packed[r0:r1], np.asarray(w.scales).reshape(w.n, w.k // 32)[r0:r1], r1 - r0, w.k)
+        return Mxfp4Weight(w.packed[r0:r1], np.asarray(w.scales).reshape(w.n, w.k // 32)[r0:r1], r1 - r0, w.k, dec)
     blocks_per_row = w.k // 64
     return Nf4Weight(w.packed[r0:r1], np.asarray(w.absmax).reshape(w.n, blocks_per_row)[r0:r1].reshape(-1),
-                     r1 - r0, w.k)
+                     r1 - r0, w.k, dec)
 
 
 @dataclass

@@ -525,3 +525,15 @@ def test_cfg_step_varlen_with_full_lengths_is_the_batched_step():
     b = O.cfg_step(text, z, [0.6, 0.6], 0.125, 4.0, cond, unc, 2, 2, O.TINY)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nf4"])
+def test_predecoded_block_is_the_same_block(fmt):
+    """Attaching the decoded weight values changes no result bit."""
+    rng = np.random.default_rng(61)
+    w = _tiny_block(rng, fmt)
+    x = N.bf16_round(rng.normal(0, 1, (1, 2 + 4, 512)))
+    c = rng.normal(0, 1, (1, 512))
+    a = O.block_forward(x, c, w, 2, 2, 2, O.TINY)
+    b = O.block_forward(x, c, O.predecode(w), 2, 2, 2, O.TINY)
+    assert np.array_equal(a, b)
