@@ -283,14 +283,22 @@ int sfm_cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sf
                  const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
                  int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream);
 
-/* sfm_cfg_step with launch timing, for measuring the gate/up projection inside
- * a timed step.  ev_begin[i] / ev_end[i] are HIP events (hipEvent_t, created
- * and owned by the caller) that are recorded on `stream` immediately before and
- * after the i-th gate/up projection launch of the step (conditional layers
- * first, then unconditional), for i < n_events; later launches are not
- * bracketed.  The two passes run one after the other on `stream` here, so that
- * each bracketed launch has the GPU to itself.  *n_recorded (if not NULL) receives the number of pairs recorded.
- * Errors as sfm_cfg_step, plus SFM_E_INVALID_ARG for NULL events. */
+/* sfm_cfg_step with launch timing, for measuring the matrix kernels inside a
+ * timed step.  ev_begin[i] / ev_end[i] are HIP events (hipEvent_t, created and
+ * owned by the caller) recorded on `stream` immediately before and after the
+ * i-th matrix launch of the step, for i < n_events; later launches are not
+ * bracketed.  Every block contributes five launches in this order: QKV
+ * projection, attention, output projection, gate/up projection, down
+ * projection; the conditional pass's layers come first, then the
+ * unconditional pass's (pair (p * layers + l) * 5 + j for pass p, layer l,
+ * launch j).  The two passes run one after the other on `stream` here, so
+ * that each bracketed launch has the GPU to itself, and every kernel takes the
+ * launch shape it uses when it runs alone (as in sfm_block_forward: attention
+ * on one persistent workgroup per compute unit, projection tiles chosen by
+ * whole rounds of workgroups); sfm_cfg_step's concurrent passes instead take
+ * the shapes that share the GPU best.  *n_recorded (if not NULL) receives the number of
+ * pairs recorded.  Errors as sfm_cfg_step, plus SFM_E_INVALID_ARG for NULL
+ * events. */
 int sfm_cfg_step_timed(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_model_weights* uncond,
                        const uint16_t* text, const float* z, float* z_out, float t, float dt, float guidance, int B,
                        int T, int gh, int gw, float* v_c_out, float* v_u_out, void* ws, size_t ws_bytes, void* stream,

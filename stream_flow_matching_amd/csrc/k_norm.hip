@@ -193,15 +193,20 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(const uint16_t*
     quant_store_row<MAXC>(v, nchunk, amax, q + m * cols, s + m);
 }
 
-// out[b][n] = sum_k w[n][k] * act(in[b][k]) + bias[n]; each wave computes
-// kGemvR consecutive output rows (their weight rows in flight together),
-// act = SiLU or identity; k % 8 == 0, B <= kGemvB.
+// out_l[b][n] = sum_k w_l[n][k] * act(in[b][k]) + bias_l[n] for the layers l
+// of the grid's y dimension (weights and biases by pointer per layer, outputs
+// out + l * out_stride); each wave computes kGemvR consecutive output rows
+// (their weight rows in flight together), act = SiLU or identity; k % 8 == 0,
+// B <= kGemvB.
 constexpr int kGemvB = 8;
 constexpr int kGemvR = 4;
-__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ in, int act_silu,
-                                                   const uint16_t* __restrict__ w, const float* __restrict__ bias,
-                                                   float* __restrict__ out, int B, int n_out, int k) {
+__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ in, int act_silu, GemvLayers p,
+                                                   float* __restrict__ out, int64_t out_stride, int B, int n_out,
+                                                   int k) {
     extern __shared__ float xin[];  // [B][k]
+    const uint16_t* __restrict__ w = p.w[blockIdx.y];
+    const float* __restrict__ bias = p.bias[blockIdx.y];
+    out += (int64_t)blockIdx.y * out_stride;
     for (int i = threadIdx.x; i < B * k; i += 256) {
         const float t = in[i];
         xin[i] = act_silu ? t / (1.0f + expf(-t)) : t;
@@ -268,10 +273,18 @@ __global__ void timestep_embed_kernel(float t, float* e, int B, int dim) {
 
 hipError_t launch_gemv(const float* in, int act_silu, const uint16_t* w, const float* bias, float* out, int B,
                        int n_out, int k, hipStream_t st) {
-    if (B > kGemvB) return hipErrorInvalidValue;
+    GemvLayers p{};
+    p.w[0] = w;
+    p.bias[0] = bias;
+    return launch_gemv_layers(in, act_silu, p, 1, out, 0, B, n_out, k, st);
+}
+
+hipError_t launch_gemv_layers(const float* in, int act_silu, const GemvLayers& p, int layers, float* out,
+                              int64_t out_stride, int B, int n_out, int k, hipStream_t st) {
+    if (B > kGemvB || layers < 1 || layers > kGemvMaxLayers) return hipErrorInvalidValue;
     const size_t shm = (size_t)B * k * sizeof(float);
-    hipLaunchKernelGGL(gemv_kernel, dim3((n_out + 4 * kGemvR - 1) / (4 * kGemvR)), dim3(256), shm, st, in, act_silu, w,
-                       bias, out, B, n_out, k);
+    hipLaunchKernelGGL(gemv_kernel, dim3((n_out + 4 * kGemvR - 1) / (4 * kGemvR), layers), dim3(256), shm, st, in,
+                       act_silu, p, out, out_stride, B, n_out, k);
     return hipGetLastError();
 }
 

@@ -250,8 +250,9 @@ hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa,
         if (e_ != hipSuccess) return fail(SFM_E_DEVICE, "launch %s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
-// Caller-owned HIP events recorded around the gate/up projection launches
-// (sfm_cfg_step_timed); pairs are used in launch order until they run out.
+// Caller-owned HIP events recorded around the five matrix launches of every block (QKV,
+// attention, output, gate/up, down; sfm_cfg_step_timed); pairs are used in launch order until
+// they run out.
 struct LaunchTimer {
     void* const* begin;
     void* const* end;
@@ -262,49 +263,57 @@ struct LaunchTimer {
 // Enqueue one block; arguments already checked.  shared: another pass runs on the GPU at the
 // same time (the guided step), so attention takes one workgroup per query block, which the
 // hardware interleaves with the other pass's work, instead of the balanced persistent grid.
+// mod_pre: the block's modulation vectors [B][4D], already computed (the model computes all
+// layers' at once), or NULL to compute them here from c.
 int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
               const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
-              LaunchTimer* timer = nullptr, bool shared = false) {
-    const bool timed = timer && timer->used < timer->n;
-    auto mark = [&](void* const* ev) -> hipError_t {
-        return timed ? hipEventRecord((hipEvent_t)ev[timer->used], st) : hipSuccess;
+              LaunchTimer* timer = nullptr, bool shared = false, const float* mod_pre = nullptr) {
+    // event pair around each of the block's five matrix launches while pairs are left
+    auto begin = [&]() -> hipError_t {
+        return timer && timer->used < timer->n ? hipEventRecord((hipEvent_t)timer->begin[timer->used], st)
+                                               : hipSuccess;
     };
+    auto end = [&]() -> hipError_t {
+        if (!timer || timer->used >= timer->n) return hipSuccess;
+        return hipEventRecord((hipEvent_t)timer->end[timer->used++], st);
+    };
+#define SFM_TIMED(expr)          \
+    do {                         \
+        SFM_LAUNCH(begin());     \
+        SFM_LAUNCH(expr);        \
+        SFM_LAUNCH(end());       \
+    } while (0)
     const sfm_dims* d = &ctx->dims;
     const int L = T + gh * gw, M = B * L, D = d->emb_dim, F = d->intermediate, H = d->num_heads;
     const int64_t ms = 4 * (int64_t)D;
     BlockWs b = plan_block(d, B, T, gh, gw, fmt, ws);
-    SFM_LAUNCH(launch_gemv(c, 1, w->mod_w, w->mod_b, b.mod, B, 4 * D, d->adaln_dim, st));
+    const float* mod = mod_pre ? mod_pre : b.mod;
+    if (!mod_pre) SFM_LAUNCH(launch_gemv(c, 1, w->mod_w, w->mod_b, b.mod, B, 4 * D, d->adaln_dim, st));
     if (fmt == SFM_W_FP8_E4M3) {
-        SFM_LAUNCH(launch_adaln_fp8(x_in, L, 0, L, b.mod, ms, b.hq, b.hs, B, D, d->eps, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st, shared));
+        SFM_LAUNCH(launch_adaln_fp8(x_in, L, 0, L, mod, ms, b.hq, b.hs, B, D, d->eps, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st, shared));
     } else {
-        SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, b.mod, ms, b.h, B, D, d->eps, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, mod, ms, b.h, B, D, d->eps, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
     }
     SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T, gh,
                                    gw, H, d->eps, lens, st));
-    SFM_LAUNCH(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
+    SFM_TIMED(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
     if (fmt == SFM_W_FP8_E4M3) {
         SFM_LAUNCH(launch_quant_rows(b.o, M, D, b.oq, b.os, st));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, b.mod + D, ms, M, L, st, shared));
-        SFM_LAUNCH(launch_adaln_fp8(x_out, L, 0, L, b.mod + 2 * D, ms, b.hq, b.hs, B, D, d->eps, st));
-        SFM_LAUNCH(mark(timed ? timer->begin : nullptr));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st, shared));
-        SFM_LAUNCH(mark(timed ? timer->end : nullptr));
-        if (timed) ++timer->used;
+        SFM_TIMED(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->o, x_out, x_in, mod + D, ms, M, L, st, shared));
+        SFM_LAUNCH(launch_adaln_fp8(x_out, L, 0, L, mod + 2 * D, ms, b.hq, b.hs, B, D, d->eps, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_SWIGLU, b.hq, b.hs, &w->gate_up, s, nullptr, nullptr, 0, M, L, st, shared));
         SFM_LAUNCH(launch_quant_rows(s, M, F, b.oq, b.os, st));
-        SFM_LAUNCH(
-            gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st, shared));
+        SFM_TIMED(gemm(ctx, SFM_EPI_RESID_GATE, b.oq, b.os, &w->down, x_out, x_out, mod + 3 * D, ms, M, L, st, shared));
     } else {
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, b.o, nullptr, &w->o, x_out, x_in, b.mod + D, ms, M, L, st));
-        SFM_LAUNCH(launch_adaln_bf16(x_out, L, 0, L, b.mod + 2 * D, ms, b.h, B, D, d->eps, st));
-        SFM_LAUNCH(mark(timed ? timer->begin : nullptr));
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_SWIGLU, b.h, nullptr, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
-        SFM_LAUNCH(mark(timed ? timer->end : nullptr));
-        if (timed) ++timer->used;
-        SFM_LAUNCH(gemm(ctx, SFM_EPI_RESID_GATE, s, nullptr, &w->down, x_out, x_out, b.mod + 3 * D, ms, M, L, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_RESID_GATE, b.o, nullptr, &w->o, x_out, x_in, mod + D, ms, M, L, st));
+        SFM_LAUNCH(launch_adaln_bf16(x_out, L, 0, L, mod + 2 * D, ms, b.h, B, D, d->eps, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_SWIGLU, b.h, nullptr, &w->gate_up, s, nullptr, nullptr, 0, M, L, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_RESID_GATE, s, nullptr, &w->down, x_out, x_out, mod + 3 * D, ms, M, L, st));
     }
+#undef SFM_TIMED
     return SFM_OK;
 }
 
@@ -315,6 +324,7 @@ struct StepWs {
     uint16_t* x;
     float* sf;
     uint16_t* hf;
+    float* mods;  // modulation vectors of up to kGemvMaxLayers layers [layer][B][4D]
     void* block;
     size_t bytes;
 };
@@ -329,6 +339,7 @@ StepWs plan_model(const sfm_dims* d, int B, int T, int gh, int gw, void* base) {
     w.x = c.take<uint16_t>(B * L * D);
     w.sf = c.take<float>(B * D);
     w.hf = c.take<uint16_t>(B * N * D);
+    w.mods = c.take<float>(kGemvMaxLayers * B * 4 * D);
     const size_t blk = plan_block(d, B, T, gh, gw, SFM_W_FP8_E4M3, nullptr).bytes;
     w.block = c.take<char>(blk);
     w.bytes = c.off + 256;
@@ -436,9 +447,20 @@ int run_model(const sfm_context* ctx, const sfm_model_weights* mw, const uint16_
     SFM_LAUNCH(launch_gemv(w.hdn, 1, mw->t_w2, mw->t_b2, w.c, B, A, A, st));
     if (T > 0) SFM_LAUNCH(launch_copy_rows(text, T, w.x, L, B, T, D, st));
     SFM_LAUNCH(launch_small_linear(latent, 0, B * (int64_t)N, 0, 0, mw->x_w, mw->x_b, w.x, 1, N, L, T, B * N, D, C, st));
-    for (int i = 0; i < mw->num_layers; ++i)
-        SFM_CHECK(
-            run_block(ctx, &mw->blocks[i], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st, lens, timer, shared));
+    // every layer's modulation comes from the same c: one product per run of up to kGemvMaxLayers layers
+    const int64_t mstride = (int64_t)B * 4 * D;
+    for (int i0 = 0; i0 < mw->num_layers; i0 += kGemvMaxLayers) {
+        const int nl = std::min(kGemvMaxLayers, mw->num_layers - i0);
+        GemvLayers p{};
+        for (int l = 0; l < nl; ++l) {
+            p.w[l] = mw->blocks[i0 + l].mod_w;
+            p.bias[l] = mw->blocks[i0 + l].mod_b;
+        }
+        SFM_LAUNCH(launch_gemv_layers(w.c, 1, p, nl, w.mods, mstride, B, 4 * D, A, st));
+        for (int l = 0; l < nl; ++l)
+            SFM_CHECK(run_block(ctx, &mw->blocks[i0 + l], SFM_W_FP8_E4M3, w.x, w.x, w.c, B, T, gh, gw, w.block, st,
+                                lens, timer, shared, w.mods + l * mstride));
+    }
     SFM_LAUNCH(launch_gemv(w.c, 1, mw->f_mod_w, mw->f_mod_b, w.sf, B, D, A, st));
     SFM_LAUNCH(launch_adaln_bf16(w.x, L, T, N, w.sf, D, w.hf, B, D, d->eps, st));
     SFM_LAUNCH(launch_small_linear(w.hf, 1, B * (int64_t)N, 0, 0, mw->f_w, mw->f_b, v_out, 0, B * (int64_t)N, 0, 0,
@@ -1017,9 +1039,10 @@ int cfg_step(const sfm_context* ctx, const sfm_model_weights* cond, const sfm_mo
     if (v_u_out) vu = v_u_out;
     const hipStream_t st = (hipStream_t)stream;
     if (timer) {
-        // one pass after the other on the caller's stream, so that each timed launch runs alone
-        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, lp, timer, true));
-        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, nullptr, timer, true));
+        // one pass after the other on the caller's stream, so that each timed launch runs alone, with
+        // the launch shapes a kernel takes when it has the GPU to itself
+        SFM_CHECK(run_model(ctx, cond, text, z, t, vc, B, T, gh, gw, mws_c, st, lp, timer, false));
+        SFM_CHECK(run_model(ctx, uncond, nullptr, z, t, vu, B, 0, gh, gw, mws_u, st, nullptr, timer, false));
     } else {
         // the passes are independent: each on its own stream, so that the last, partly filled
         // round of workgroups of one pass's kernels shares the GPU with the other pass

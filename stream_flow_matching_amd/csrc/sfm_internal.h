@@ -150,8 +150,18 @@ int fail(int code, const char* fmt, ...);
 // All launchers enqueue on `st` and return hipError_t of the launch.
 
 // k_norm.hip
+// out[b][n] = sum_k w[n][k] act(in[b][k]) + bias[n] (act SiLU when act_silu); B <= 8, k % 8 == 0
 hipError_t launch_gemv(const float* in, int act_silu, const uint16_t* w, const float* bias, float* out, int B,
                        int n_out, int k, hipStream_t st);
+// The same product for `layers` weight sets at once (one launch): layer l reads p.w[l], p.bias[l]
+// (bias may be NULL) and writes out + l * out_stride.
+constexpr int kGemvMaxLayers = 64;
+struct GemvLayers {
+    const uint16_t* w[kGemvMaxLayers];
+    const float* bias[kGemvMaxLayers];
+};
+hipError_t launch_gemv_layers(const float* in, int act_silu, const GemvLayers& p, int layers, float* out,
+                              int64_t out_stride, int B, int n_out, int k, hipStream_t st);
 hipError_t launch_adaln_fp8(const uint16_t* x, int64_t rows_per_batch_in, int64_t row_off, int rows_per_batch,
                             const float* scale, int64_t scale_stride, uint8_t* hq, float* hs, int B, int D, float eps,
                             hipStream_t st);

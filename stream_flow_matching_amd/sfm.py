@@ -304,9 +304,10 @@ def sfm_cfg_step(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, 
 
 def sfm_cfg_step_timed(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, t, dt, guidance, B, T, gh, gw,
                        ws, ev_begin, ev_end, v_c_out=None, v_u_out=None, stream=None):
-    """sfm_cfg_step with torch.cuda.Event pairs recorded around the gate/up
-    projection launches (the events must have been recorded once, so that
-    their HIP handles exist).  Returns the number of pairs recorded."""
+    """sfm_cfg_step with torch.cuda.Event pairs recorded around the five matrix
+    launches of every block (QKV, attention, output, gate/up, down; the events
+    must have been recorded once, so that their HIP handles exist).  Returns the
+    number of pairs recorded."""
     n = min(len(ev_begin), len(ev_end))
     arr = ctypes.c_void_p * max(n, 1)
     b = arr(*[ctypes.c_void_p(e.cuda_event) for e in ev_begin[:n]])
