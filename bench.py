@@ -52,6 +52,10 @@ def parse():
                     help="print per-kernel counter tables and the traffic records from rocprofv3 --pmc passes "
                          "over --pmc-probe (one output directory per pass) and exit (no GPU needed)")
     ap.add_argument("--no-hbm", action="store_true", help="skip the bandwidth-bound kernels with flushed caches")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="time the vendor libraries at this path's shapes (hipBLASLt FP8 through torch._scaled_mm, "
+                         "bf16 torch.mm, torch's scaled_dot_product_attention) and exit; a context figure, not part "
+                         "of the path")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel tables (markdown) from a rocprofv3 --kernel-trace --stats output "
                          "directory of this script and exit (no GPU needed)")
@@ -335,7 +339,7 @@ def roofline(table, w):
             "per_kernel": table}
 
 
-def hbm_kernels(sfm, synth, ctx, iters=5):
+def hbm_kernels(sfm, synth, ctx, iters=5, warm=True):
     """The bandwidth-bound kernels at the 1024^2 conditional shape (M 4608), each
     launched alone after a FLUSH_BYTES write that evicts the Infinity Cache and the
     L2s, timed with HIP events on the launch stream.  Bytes are algorithmic: each
@@ -383,7 +387,8 @@ def hbm_kernels(sfm, synth, ctx, iters=5):
     out = []
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for name, shape, nbytes, fn in cases:
-        fn()
+        if warm:
+            fn()
         tot = 0.0
         for it in range(iters):
             flush.fill_(it & 0xFF)
@@ -416,7 +421,7 @@ def pmc_probe(sfm, synth, ctx):
     torch.cuda.synchronize()
     del cond, unc, cm, um, ws
     torch.cuda.empty_cache()
-    hbm_kernels(sfm, synth, ctx, iters=1)
+    hbm_kernels(sfm, synth, ctx, iters=1, warm=False)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -494,7 +499,8 @@ def pmc_summary(dirs):
             elif "copyBuffer" in r["Kernel_Name"]:
                 group_of[did] = ("copy", "")
             elif "sfm::" in r["Kernel_Name"] and int(did) > last_step:
-                group_of[did] = (_short(r["Kernel_Name"]), "alone")
+                wg = int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1)
+                group_of[did] = (f"{_short(r['Kernel_Name'])} [{wg} wg]", "alone")
         for r in rows:
             g = group_of.get(r["Dispatch_Id"])
             if not g:
@@ -517,6 +523,31 @@ def pmc_summary(dirs):
         print()
         print("Byte-counter scales from the copy of %d MiB: %s." % (COPY_BYTES >> 20, ", ".join(
             f"{c} x {v:.4f} KiB -> bytes" for c, v in sorted(scale.items()))))
+    # derived per kernel: matrix-core utilisation, counted matrix FLOPs against the algorithmic
+    # ones, LDS bank conflicts per LDS-active cycle, and bytes against the algorithmic bytes
+    print()
+    print("| kernel | pass | MfmaUtil (%) | matrix FLOP counted / algorithmic | LDS conflict cycles / active "
+          "| FETCH + WRITE (MB, scaled) | algorithmic (MB) | ratio |")
+    print("|---|---|---|---|---|---|---|---|")
+    Lof = {"cond": 4608, "uncond": 4096}
+    for g, cv in sorted(vals.items()):
+        util = f"{mean(cv['MfmaUtil']):.1f}" if "MfmaUtil" in cv else ""
+        flop_ratio = conf = traffic = alg = ratio = ""
+        if g[0] in KINDS:
+            fl, ab = kernel_work(g[0], Lof[g[1]])
+            mops = sum(mean(cv[c]) for c in cv if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+            if mops:
+                flop_ratio = f"{mops * 512 / fl:.3f}"
+            alg = f"{ab / 1e6:.1f}"
+        if "SQ_LDS_BANK_CONFLICT" in cv and "SQ_LDS_IDX_ACTIVE" in cv and mean(cv["SQ_LDS_IDX_ACTIVE"]) > 0:
+            conf = f"{mean(cv['SQ_LDS_BANK_CONFLICT']) / mean(cv['SQ_LDS_IDX_ACTIVE']):.3f}"
+        if "FETCH_SIZE" in cv and "WRITE_SIZE" in cv and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+            tb = (mean(cv["FETCH_SIZE"]) * scale["FETCH_SIZE"] + mean(cv["WRITE_SIZE"]) * scale["WRITE_SIZE"]) * 1024
+            traffic = f"{tb / 1e6:.1f}"
+            if g[0] in KINDS:
+                ratio = f"{tb / kernel_work(g[0], Lof[g[1]])[1]:.2f}"
+        if util or flop_ratio or conf or traffic:
+            print(f"| `{g[0]}` | {g[1]} | {util} | {flop_ratio} | {conf} | {traffic} | {alg} | {ratio} |")
     for g, cv in sorted(vals.items()):
         if g[0] in KINDS and "FETCH_SIZE" in cv and "WRITE_SIZE" in cv and "FETCH_SIZE" in scale:
             fb = mean(cv["FETCH_SIZE"]) * 1024 * scale["FETCH_SIZE"]
@@ -576,6 +607,35 @@ def trace_summary(out_dir):
             if "sfm::" in r["Name"]:
                 print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                       f"{float(r['Percentage']):.2f} |")
+
+
+def yardstick(iters=20):
+    """Vendor-library timings at the step's shapes on this GPU, for context: hipBLASLt's FP8
+    GEMM (torch._scaled_mm, per-tensor scales, bf16 out, no fused epilogue), torch's bf16 GEMM
+    and torch's scaled_dot_product_attention at one pass's attention shape."""
+    import torch
+    out = {}
+    for name, (M, N, K) in (("gate_up", (4608, 24576, 4608)), ("o", (4608, 4608, 4608)),
+                            ("down", (4608, 4608, 12288)), ("qkv", (4608, 13824, 4608)),
+                            ("square_8192", (8192, 8192, 8192))):
+        a = (torch.randn(M, K, device="cuda") * 0.5).to(torch.float8_e4m3fn)
+        b = (torch.randn(N, K, device="cuda") * 0.5).to(torch.float8_e4m3fn).t()
+        one = torch.tensor(1.0, device="cuda")
+        us = time_gpu(lambda: torch._scaled_mm(a, b, scale_a=one, scale_b=one, out_dtype=torch.bfloat16), iters) * 1e6
+        ab = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        bb = torch.randn(K, N, device="cuda", dtype=torch.bfloat16)
+        us16 = time_gpu(lambda: ab @ bb, iters) * 1e6
+        fl = 2.0 * M * N * K
+        out[name] = {"shape": [M, N, K], "fp8_scaled_mm_us": round(us, 1),
+                     "fp8_frac": round(fl / us / 1e6 / FP8_PEAK_TFLOPS, 4), "bf16_mm_us": round(us16, 1),
+                     "bf16_frac": round(fl / us16 / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    for L in (4608, 4096):
+        q = torch.randn(1, 18, L, 256, device="cuda", dtype=torch.bfloat16)
+        k, v = torch.randn_like(q), torch.randn_like(q)
+        us = time_gpu(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), 10) * 1e6
+        fl = 4.0 * L * L * 256 * 18
+        out[f"sdpa_{L}"] = {"us": round(us, 1), "bf16_frac": round(fl / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps({"yardstick": out}))
 
 
 def cpu_info():
@@ -668,6 +728,9 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.yardstick:
+        yardstick()
+        return
     ctx = sfm.Context("ideogram4", 0)
     if args.pmc_probe:
         pmc_probe(sfm, synth, ctx)
