@@ -70,7 +70,7 @@ typedef struct sfm_context sfm_context;
  * table for every integer position the shape limits allow, built on the host
  * in double precision and rounded to fp32, and the NF4 codebook.  Only
  * emb_dim = num_heads * 256 with head_dim 256, rope_dims 128 and
- * sum(mrope_section) = 64 are supported (else SFM_E_SHAPE).  It also creates
+ * mrope_section (24, 20, 20) are supported (else SFM_E_SHAPE).  It also creates
  * the two streams and three events on which sfm_cfg_step runs its two passes
  * side by side.  The tables never change afterwards and the context may be
  * shared by threads. */

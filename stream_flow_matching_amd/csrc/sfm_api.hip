@@ -83,10 +83,9 @@ int check_dims(const sfm_dims* d) {
     if (!d) return fail(SFM_E_INVALID_ARG, "dims is NULL");
     if (d->head_dim != 256 || d->num_heads < 1 || d->emb_dim != d->num_heads * 256)
         return fail(SFM_E_SHAPE, "need head_dim 256 and emb_dim = num_heads * 256");
-    if (d->rope_dims != 128 || d->mrope_section[0] + d->mrope_section[1] + d->mrope_section[2] != 64 ||
-        d->mrope_section[0] < 0 || d->mrope_section[1] < 0 || d->mrope_section[2] < 0 ||
-        (d->mrope_section[0] & 1) || (d->mrope_section[1] & 1))
-        return fail(SFM_E_SHAPE, "need rope_dims 128 and even mrope sections summing to 64");
+    // the rotary kernel selects the axis of pair j with the fixed boundaries 24 and 44
+    if (d->rope_dims != 128 || d->mrope_section[0] != 24 || d->mrope_section[1] != 20 || d->mrope_section[2] != 20)
+        return fail(SFM_E_SHAPE, "need rope_dims 128 and mrope_section (24, 20, 20)");
     if (d->intermediate <= 0 || d->intermediate % 256)
         return fail(SFM_E_SHAPE, "intermediate must be a positive multiple of 256");
     if (d->adaln_dim <= 0 || d->adaln_dim % 8 || d->adaln_dim > 2048)

@@ -84,6 +84,10 @@ def test_bad_dims_rejected(S):
     d = S.lib().sfm_dims_ideogram4()
     d.mrope_section[2] = 18
     assert S.sfm_check_shape(d, 1, 512, 64, 64) == -2
+    # another split of the 64 pairs: the rotary kernel's axis boundaries are fixed at 24 and 44
+    d = S.lib().sfm_dims_ideogram4()
+    d.mrope_section[0], d.mrope_section[1] = 20, 24
+    assert S.sfm_check_shape(d, 1, 512, 64, 64) == -2
 
 
 def test_positions_helper(S):
