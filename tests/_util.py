@@ -86,3 +86,27 @@ def check_rel(tag, got, ref, bar) -> float:
             f.write(json.dumps({"test": tag, "rel_l2": err, "bar": bar}) + "\n")
     assert err < bar, f"{tag}: rel-L2 {err:.3e} >= {bar}"
     return err
+
+
+def check_spread(tag, got, ref, ref_alt, factor) -> float:
+    """rel-L2 of got against the oracle's ref, bounded by `factor` times the
+    oracle's own spread: the rel-L2 between ref and ref_alt, the oracle run on
+    an input moved at rounding level (t by one float32 ulp).  Past a depth at
+    which such a change already moves the output by percents (per-token FP8
+    codes flip at their rounding boundaries and the flips compound from block
+    to block), an implementation that rounds differently cannot come closer to
+    the oracle than the oracle comes to itself; a wrong term still lands far
+    outside.  Reported like check_rel."""
+    import json
+    import os
+    import sys
+    err, spread = rel_l2(got, ref), rel_l2(ref_alt, ref)
+    bar = factor * spread
+    print(f"[margin] {tag}: rel-L2 {err:.3e} (oracle spread {spread:.3e}, bar {bar:.3e})", file=sys.stderr,
+          flush=True)
+    path = os.environ.get("SFM_MARGINS")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": tag, "rel_l2": err, "oracle_spread": spread, "bar": bar}) + "\n")
+    assert err < bar, f"{tag}: rel-L2 {err:.3e} >= {factor} x oracle spread {spread:.3e}"
+    return err
