@@ -453,6 +453,16 @@ int sfm_sample_varlen(const sfm_context* ctx, const sfm_model_weights* cond, con
 const char* sfm_status_string(int status);
 const char* sfm_last_error(void);
 
+/* Debug mode for callers hunting an asynchronous failure: with on != 0 every
+ * kernel launch of every entry point is followed by hipDeviceSynchronize and
+ * hipGetLastError, and a failure there is returned as SFM_E_DEVICE by the
+ * entry point whose launch caused it (with the launch named in
+ * sfm_last_error()).  Process-wide; off by default, or on when the
+ * environment holds SFM_SYNC_CHECK=1 as the library loads.  It serialises all
+ * streams and must stay off under HIP graph capture.  Returns the previous
+ * setting. */
+int sfm_set_sync_check(int on);
+
 #ifdef __cplusplus
 }
 #endif

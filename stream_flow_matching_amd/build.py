@@ -68,5 +68,58 @@ def build(verbose=False) -> str:
     return OUT
 
 
+# A second copy of the library whose host code carries AddressSanitizer and
+# UndefinedBehaviorSanitizer instrumentation: the sources holding the C ABI's
+# argument, shape and workspace checks and the sampler's host schedules are
+# recompiled with the host-only sanitizer options; the kernel objects of the
+# normal build are linked unchanged (device code is never instrumented).  The
+# copy is loaded only by processes that preload the sanitizer runtime.
+SAN_SOURCES = ("sfm_api.hip", "sfm_sampler.hip")
+SAN_FLAGS = ("-O1 -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+             "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer").split()
+SAN_LINK = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -shared-libsan".split()
+SAN_OUT = os.path.join(HERE, "libsfm_asan.so")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*",
+                                         "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to hipcc")
+    return hits[-1]
+
+
+def build_sanitized() -> str:
+    """Build libsfm_asan.so from the objects of build() and host-instrumented
+    copies of SAN_SOURCES."""
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources()]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    san_dir = os.path.join(BUILD, "asan")
+    os.makedirs(san_dir, exist_ok=True)
+    plain = [f for f in FLAGS if f != "-O3"]
+    linked = []
+    for src in sources():
+        name = os.path.basename(src)
+        if name not in SAN_SOURCES:
+            linked.append(os.path.join(BUILD, name + ".o"))
+            continue
+        obj = os.path.join(san_dir, name + ".o")
+        r = subprocess.run([HIPCC, *plain, *SAN_FLAGS, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized) failed for {src}:\n{r.stderr}")
+        linked.append(obj)
+    tmp = SAN_OUT + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_LINK, "-o", tmp, *linked],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_sanitized())

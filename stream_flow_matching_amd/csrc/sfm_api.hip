@@ -1,9 +1,11 @@
 // C ABI of the library: argument checking, context set-up (constant tables),
 // workspace planning and the launch sequences of the block, the velocity model
 // and the guided Euler step.  Every check runs before the first enqueue.
+#include <atomic>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -243,9 +245,23 @@ hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa,
                            gate, gs, M, w->n, w->k, L, st);
 }
 
+// Debug mode (sfm_set_sync_check, or SFM_SYNC_CHECK=1 in the environment when the library
+// loads): every launch is followed by a device-wide synchronisation and an error check, so an
+// asynchronous failure is reported by the entry point whose launch caused it.
+std::atomic<int> g_sync_check{[] {
+    const char* e = getenv("SFM_SYNC_CHECK");
+    return e && e[0] == '1' ? 1 : 0;
+}()};
+
+hipError_t after_launch(hipError_t e) {
+    if (e != hipSuccess || !g_sync_check.load(std::memory_order_relaxed)) return e;
+    e = hipDeviceSynchronize();
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
 #define SFM_LAUNCH(expr)                                                                              \
     do {                                                                                              \
-        hipError_t e_ = (expr);                                                                       \
+        hipError_t e_ = after_launch(expr);                                                           \
         if (e_ != hipSuccess) return fail(SFM_E_DEVICE, "launch %s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
@@ -564,6 +580,8 @@ const char* sfm_status_string(int s) {
 }
 
 const char* sfm_last_error(void) { return g_err.c_str(); }
+
+int sfm_set_sync_check(int on) { return g_sync_check.exchange(on ? 1 : 0); }
 
 int sfm_check_shape(const sfm_dims* dims, int B, int T, int gh, int gw) {
     SFM_CHECK(check_dims(dims));

@@ -123,6 +123,7 @@ SIGNATURES = {
     "sfm_preset_schedule": (_I, [_I, _I, _I, _P, _P, _I]),
     "sfm_sample": (_I, [_P, ctypes.POINTER(sfm_model_weights), ctypes.POINTER(sfm_model_weights), _P, _P, _P, _P,
                         _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "sfm_set_sync_check": (_I, [_I]),
     "sfm_status_string": (ctypes.c_char_p, [_I]),
     "sfm_last_error": (ctypes.c_char_p, []),
 }
@@ -426,3 +427,8 @@ def sfm_sample(ctx, cond: ModelWeights, uncond: ModelWeights, text, z, z_out, t,
 def workspace(nbytes, device="cuda"):
     """A caller-owned workspace tensor of at least nbytes."""
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def sfm_set_sync_check(on):
+    """Debug mode: synchronise and check for errors after every launch; returns the previous setting."""
+    return lib().sfm_set_sync_check(1 if on else 0)

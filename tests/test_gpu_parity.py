@@ -519,6 +519,23 @@ def test_block_tiny_batch2_ragged(sfm, ctx_tiny):
     check_rel("test_block_tiny_batch2_ragged#2", np64(xo) - np64(x), ref - np64(x), UPDATE_BAR["fp8"])
 
 
+def test_sync_check_mode_changes_nothing(sfm, ctx_tiny):
+    """The debug mode (a device synchronisation and error check after every launch)
+    gives the same block output bit for bit, and the setter reports the previous mode."""
+    _say("sync-check mode")
+    w = synth.WORKLOADS["tiny_block"]
+    p = synth.block_params(w.shape, (5, w.name), "fp8")
+    x, c = synth.block_inputs(w)
+    plain = _run_block(sfm, ctx_tiny, w, p, x, c)
+    prev = sfm.sfm_set_sync_check(True)
+    try:
+        checked = _run_block(sfm, ctx_tiny, w, p, x, c)
+        assert sfm.sfm_set_sync_check(True) == 1
+    finally:
+        sfm.sfm_set_sync_check(prev)
+    assert torch.equal(plain, checked)
+
+
 def test_block_gate_zero_is_identity(sfm, ctx_tiny):
     _say("block gate zero")
     w = synth.WORKLOADS["tiny_block"]
