@@ -78,6 +78,195 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SFM_LDS(lds), 16, voff, soff, 0, 0);
 }
 
+// QKV epilogue with QK-RMSNorm and the rotary embedding folded in (launch_gemm_fp8_qkv_rope)
+constexpr int kEpiQkvRope = 4;
+
+// The epilogue of a wave's 128 x 128 accumulator block (acc[i][j][r] = row 32 i + (l & 31),
+// column 32 j + 8 (r >> 2) + 4 (l >> 5) + (r & 3), as in gemm_epilogue_lds) of a 256 x 256 tile
+// of the QKV output: with 256-column tiles, tile column tn is head tn % H of q, k or v
+// (part tn / H), and the wave holds columns wn 128 .. wn 128 + 127 of that head.  Every value
+// is first rounded to bf16 (the projection's output precision).
+//   q, k: the row's sum of squares over the head (the lane, its partner lane l ^ 32, then the
+//     other column wave through `xch` in LDS), u / sqrt(mean(u^2) + eps) * gamma, and for the
+//     dims j < 64 / j + 64 of wave 0 the rotation of pair j (the partner of fragment column j
+//     is fragment column j + 2 of the same lane) by the row's position on pair j's axis; bf16
+//     rows staged through the wave's LDS region and stored as 16-byte chunks at
+//     q / k[b][h][l][d].
+//   v: fp16 (saturated at +-65504), transposed through LDS into [d][token] in the stored key
+//     order of vt_slot and stored as 16-byte chunks of V^T[b][h][d][l] when the wave's rows are
+//     128 valid rows of one sample starting at a multiple of 32 of its sequence; otherwise each
+//     value is stored on its own.
+template <int FM, int FN>
+__device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uint8_t* lds, float* xch, int m0w,
+                                                  int wm, int wn, int tn, int lane, int M, int L, const float* rsl,
+                                                  const float* csl, const RopeArgs& ra) {
+    constexpr int TM = 32 * FM, TN = 32 * FN;
+    static_assert(TM == 128 && TN == 128, "a 256 x 256 tile: one head per tile column");
+    const int lc = lane & 31, lg = lane >> 5;
+    const int part = tn / ra.H, h = tn - part * ra.H;
+    float rs[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) rs[i] = rsl[32 * i + lc];
+    // the projection's output values (bf16, the STORE epilogue's rounding) of accumulator
+    // elements (i, j, 4 q .. 4 q + 3)
+    auto y4 = [&](int i, int j, int q) {
+        const v4f cs = *reinterpret_cast<const v4f*>(csl + 32 * j + 8 * q + 4 * lg);
+        const uint32_t lo = cvt_bf16x2(acc[i][j][4 * q] * rs[i] * cs[0], acc[i][j][4 * q + 1] * rs[i] * cs[1]);
+        const uint32_t hi = cvt_bf16x2(acc[i][j][4 * q + 2] * rs[i] * cs[2], acc[i][j][4 * q + 3] * rs[i] * cs[3]);
+        return v4f{__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
+                   __uint_as_float(hi & 0xFFFF0000u)};
+    };
+    // the wave's rows span at most two samples (L >= 256 > TM)
+    const int b_first = min(m0w, M - 1) / L, split = (b_first + 1) * L;
+    if (part < 2) {
+        float rn[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4f u = y4(i, j, q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
+                }
+            ss += __shfl_xor(ss, 32, 64);
+            rn[i] = ss;
+            if (lg == 0) xch[(2 * wm + wn) * TM + 32 * i + lc] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            rn[i] = 1.0f / sqrtf((rn[i] + xch[(2 * wm + (wn ^ 1)) * TM + 32 * i + lc]) / 256.0f + ra.eps);
+        // the norm weights of the lane's 64 columns, loaded once (bf16 pairs)
+        const uint16_t* gam = (part == 0 ? ra.qn : ra.kn) + wn * TN;
+        uint2 gw[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) gw[j][q] = *reinterpret_cast<const uint2*>(gam + 32 * j + 8 * q + 4 * lg);
+        auto gamma4 = [&](int j, int q) {
+            const uint2 g2 = gw[j][q];
+            return v4f{__uint_as_float(g2.x << 16), __uint_as_float(g2.x & 0xFFFF0000u), __uint_as_float(g2.y << 16),
+                       __uint_as_float(g2.y & 0xFFFF0000u)};
+        };
+        // bf16 rows of 128 columns: 16-byte chunk c of row r at physical chunk c ^ (r & 15)
+        auto stage = [&](int row, int ch, v4f o) {
+            *reinterpret_cast<uint2*>(lds + row * 256 + ((ch ^ (row & 15)) << 4) + lg * 8) =
+                make_uint2(cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]));
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = 32 * i + lc;
+            // wave 0: the cos / sin of the row's 32 pairs p0 .. p0 + 3 (p0 = 32 j + 8 q + 4 lg), all
+            // loads issued before any is used; four pairs share an axis (the section boundaries
+            // 24 and 44 are multiples of 4)
+            v4f cs4[FN / 2][4], sn4[FN / 2][4];
+            if (wn == 0) {
+                const int m = min(m0w + row, M - 1);
+                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
+                const int Tb = ra.varlen ? ra.lens.len[b] : ra.T;
+                const int pt = axis_pos(l, ra.T, Tb, ra.gw, 0), ph = axis_pos(l, ra.T, Tb, ra.gw, 1),
+                          pw = axis_pos(l, ra.T, Tb, ra.gw, 2);
+#pragma unroll
+                for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int p0 = 32 * j + 8 * q + 4 * lg;
+                        const int pos = p0 < 24 ? pt : (p0 < 44 ? ph : pw);
+                        cs4[j][q] = *reinterpret_cast<const v4f*>(ra.cos_t + pos * 64 + p0);
+                        sn4[j][q] = *reinterpret_cast<const v4f*>(ra.sin_t + pos * 64 + p0);
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // columns c (fragment column j) and c + 64 (fragment column j + 2)
+                    const v4f ga = gamma4(j, q), gb = gamma4(j + FN / 2, q);
+                    v4f a = y4(i, j, q), bb = y4(i, j + FN / 2, q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a[e] = a[e] * rn[i] * ga[e];
+                        bb[e] = bb[e] * rn[i] * gb[e];
+                    }
+                    if (wn == 0) {
+                        // rotation of pairs p0 .. p0 + 3 (dims c, c + 64)
+                        const v4f c = cs4[j][q], sn = sn4[j][q];
+                        v4f ra4, rb4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            ra4[e] = a[e] * c[e] - bb[e] * sn[e];
+                            rb4[e] = bb[e] * c[e] + a[e] * sn[e];
+                        }
+                        a = ra4;
+                        bb = rb4;
+                    }
+                    stage(row, 4 * j + q, a);
+                    stage(row, 4 * (j + FN / 2) + q, bb);
+                }
+        }
+        uint16_t* const dst = part == 0 ? ra.q : ra.k;
+#pragma unroll
+        for (int s = 0; s < TM * 16 / 64; ++s) {
+            const int qq = 64 * s + lane, row = qq >> 4, ch = qq & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + row * 256 + ((ch ^ (row & 15)) << 4));
+            const int m = m0w + row;
+            if (m < M) {
+                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
+                *reinterpret_cast<uint4*>(dst + (((int64_t)b * ra.H + h) * ra.Lp + l) * 256 + wn * TN + ch * 8) = v;
+            }
+        }
+    } else {
+        auto f16 = [](float v) { return (_Float16)fminf(fmaxf(v, -65504.0f), 65504.0f); };
+        const int l0 = m0w - b_first * L;
+        if (m0w + TM <= split && m0w + TM <= M && (l0 & 31) == 0) {
+            // [d][stored token] fp16 rows of 256 bytes: 16-byte chunk c of row d at physical chunk
+            // c ^ ((d >> 2) & 15); the lane's token 32 i + lc sits at 32 i + vt_slot(lc)
+            const int sl = vt_slot(lc);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f u = y4(i, j, q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int d = 32 * j + 8 * q + 4 * lg + e, t = 32 * i + sl;
+                            *reinterpret_cast<_Float16*>(lds + d * 256 + (((t >> 3) ^ ((d >> 2) & 15)) << 4) +
+                                                         (t & 7) * 2) = f16(u[e]);
+                        }
+                    }
+            uint16_t* const vt = ra.vt + ((int64_t)b_first * ra.H + h) * 256 * ra.Lp;
+#pragma unroll
+            for (int s = 0; s < TN * 16 / 64; ++s) {
+                const int qq = 64 * s + lane, d = qq >> 4, ch = qq & 15;
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + d * 256 + ((ch ^ ((d >> 2) & 15)) << 4));
+                *reinterpret_cast<uint4*>(vt + (int64_t)(wn * TN + d) * ra.Lp + l0 + ch * 8) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m0w + 32 * i + lc;
+                if (m >= M) continue;
+                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
+                _Float16* const base = reinterpret_cast<_Float16*>(ra.vt) +
+                                       (((int64_t)b * ra.H + h) * 256 + wn * TN) * ra.Lp + (l & ~31) + vt_slot(l & 31);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f u = y4(i, j, q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) base[(int64_t)(32 * j + 8 * q + 4 * lg + e) * ra.Lp] = f16(u[e]);
+                    }
+            }
+        }
+    }
+}
+
 // LDS of one configuration: the two-stage ring (also the epilogue's staging, a quarter per
 // wave), then the epilogue's scales.  WF 0: FP8 weights (128 bytes per row and stage); WF 1:
 // MXFP4 weights (64 bytes per row and stage).
@@ -98,7 +287,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t* __restrict__ A, const float* __restrict__ sa, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, const uint8_t* __restrict__ wexp, uint16_t* out, const uint16_t* resid,
     const float* __restrict__ gate, int64_t gate_stride, int M, int N, int K, int L, int ntm, int ntn, int kps,
-    float* __restrict__ part) {
+    float* __restrict__ part, RopeArgs rope) {
     constexpr bool MX = WF == 1;
     using Lds = GemmLds<BM, BN, EPI, WF>;
     constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
@@ -127,6 +316,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         klen = min(K - kbeg, kps * 256);
     }
     grouped_tile(tile, ntm, ntn, kGroupM, tm, tn);
+    // the divisions above run on the vector ALU; naming the results wave-uniform keeps the
+    // buffer descriptors and the loop bounds in scalar registers (a descriptor left in vector
+    // registers turns every direct load of the loop into a per-lane waterfall)
+    tm = __builtin_amdgcn_readfirstlane(tm);
+    tn = __builtin_amdgcn_readfirstlane(tn);
+    kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+    klen = __builtin_amdgcn_readfirstlane(klen);
     const int m0 = tm * BM;
 
     // wave-load v of this wave covers tile rows 8 (wave + 4 v) + (lane >> 3); the lane writes
@@ -339,6 +535,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         *reinterpret_cast<v4f*>(pbase + (int64_t)row * N + 32 * j + 8 * q + 4 * lg) =
                             v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
+    } else if constexpr (EPI == kEpiQkvRope) {
+        // the gate area behind the scales (unused by this epilogue) takes the row sums of squares
+        epilogue_qkv_rope<FM, FN>(acc, smem + wave * (Lds::RING / 4), scl + BM + BN, m0 + wm * TM, wm, wn, tn, lane, M,
+                                  L, scl + wm * TM, scl + BM + wn * TN, rope);
     } else {
         gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (Lds::RING / 4), m0 + wm * TM, wn, tn, lane, M, N, L,
                                                out, resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN,
@@ -376,7 +576,7 @@ template <int BM, int BN, int EPI, int WF = 0>
 hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
                       hipStream_t st, int splits = 1, int kps = 0, float* part = nullptr,
-                      const uint8_t* wexp = nullptr) {
+                      const uint8_t* wexp = nullptr, const RopeArgs& rope = RopeArgs{}) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
     // two ring stages, then the epilogue's scales (row, column and three gate rows)
@@ -385,7 +585,7 @@ hipError_t launch_cfg(const uint8_t* a, const float* sa, const uint8_t* w, const
     static std::atomic<uint64_t> lds_raised{0};
     raise_lds_limit_once((const void*)kern, shm, lds_raised);
     hipLaunchKernelGGL(kern, dim3(ntm * ntn * splits), dim3(256), shm, st, a, sa, w, sw, wexp, out, resid, gate,
-                       gate_stride, M, N, K, L, ntm, ntn, kps, part);
+                       gate_stride, M, N, K, L, ntm, ntn, kps, part, rope);
     return hipGetLastError();
 }
 
@@ -471,6 +671,13 @@ hipError_t launch_gemm_fp8(int epi, const uint8_t* a, const float* sa, const uin
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_fp8_qkv_rope(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, int M,
+                                   int K, int L, const RopeArgs& ra, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    return launch_cfg<256, 256, kEpiQkvRope>(a, sa, w, sw, nullptr, nullptr, nullptr, 0, M, 3 * ra.H * 256, K, L, st, 1,
+                                             0, nullptr, nullptr, ra);
 }
 
 hipError_t launch_gemm_mx(int epi, const uint8_t* a, const float* sa, const uint8_t* w, const uint8_t* wexp,

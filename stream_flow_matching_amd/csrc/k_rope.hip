@@ -35,17 +35,6 @@ __device__ __forceinline__ uint16_t bf16_to_f16_bits(uint16_t b) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// position on one axis of row l of a sample whose text prefix has T rows, the
-// first Tb of them real text: text (and padding) rows l -> l, image token i =
-// l - T at (Tb, Tb + i / gw, Tb + i % gw)
-__device__ __forceinline__ int axis_pos(int l, int T, int Tb, int gw, int axis) {
-    if (l < T) return l;
-    const int i = l - T;
-    if (axis == 0) return Tb;
-    if (axis == 1) return Tb + i / gw;
-    return Tb + i % gw;
-}
-
 // x of lane (l & ~15) | ((l + 8) & 15): the chunk eight 16-byte chunks away in a 16-lane row
 __device__ __forceinline__ float ror8(float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)); }
 __device__ __forceinline__ float ror_n(float x, int n) {
@@ -178,7 +167,29 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(const uint16_t* __res
     }
 }
 
+// one workgroup per (head, sample): rows [L, Lp) of q and k, and the V^T columns that hold
+// tokens [L, Lp) (inside the last partial group of 32 some of them sit before column L)
+__global__ __launch_bounds__(256) void attn_pad_zero_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                                            uint16_t* __restrict__ vt, int L, int Lp, int H) {
+    const int h = blockIdx.x, b = blockIdx.y, np = Lp - L;
+    const int64_t bh = (int64_t)b * H + h;
+    uint16_t* qr = q + (bh * Lp + L) * 256;
+    uint16_t* kr = k + (bh * Lp + L) * 256;
+    for (int i = threadIdx.x; i < np * 256; i += 256) qr[i] = kr[i] = 0;
+    for (int i = threadIdx.x; i < 256 * np; i += 256) {
+        const int d = i / np, t = L + i % np;
+        vt[(bh * 256 + d) * Lp + (t & ~31) + vt_slot(t & 31)] = 0;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_attn_pad_zero(uint16_t* q, uint16_t* k, uint16_t* vt, int B, int L, int H, hipStream_t st) {
+    const int Lp = padded_len(L);
+    if (Lp == L || B == 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_pad_zero_kernel, dim3(H, B), dim3(256), 0, st, q, k, vt, L, Lp, H);
+    return hipGetLastError();
+}
 
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const uint16_t* kn, const float* cos_t,
                                const float* sin_t, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh,

@@ -280,6 +280,26 @@ struct LaunchTimer {
 // hardware interleaves with the other pass's work, instead of the balanced persistent grid.
 // mod_pre: the block's modulation vectors [B][4D], already computed (the model computes all
 // layers' at once), or NULL to compute them here from c.
+RopeArgs rope_args(const sfm_context* ctx, const uint16_t* qn, const uint16_t* kn, uint16_t* q, uint16_t* k,
+                   uint16_t* vt, int T, int gw, int L, const TextLens* lens) {
+    RopeArgs ra{};
+    ra.q = q;
+    ra.k = k;
+    ra.vt = vt;
+    ra.qn = qn;
+    ra.kn = kn;
+    ra.cos_t = ctx->rope_cos;
+    ra.sin_t = ctx->rope_sin;
+    ra.T = T;
+    ra.gw = gw;
+    ra.Lp = padded_len(L);
+    ra.H = ctx->dims.num_heads;
+    ra.eps = ctx->dims.eps;
+    ra.varlen = lens ? 1 : 0;
+    if (lens) ra.lens = *lens;
+    return ra;
+}
+
 int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const uint16_t* x_in, uint16_t* x_out,
               const float* c, int B, int T, int gh, int gw, void* ws, hipStream_t st, const TextLens* lens = nullptr,
               LaunchTimer* timer = nullptr, bool shared = false, const float* mod_pre = nullptr) {
@@ -305,14 +325,19 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
     const float* mod = mod_pre ? mod_pre : b.mod;
     if (!mod_pre) SFM_LAUNCH(launch_gemv(c, 1, w->mod_w, w->mod_b, b.mod, B, 4 * D, d->adaln_dim, st));
     if (fmt == SFM_W_FP8_E4M3) {
+        // QKV projection with QK-RMSNorm and the rotary embedding in its epilogue: q, k and V^T
+        // go straight to the attention layouts (their padding rows zeroed apart)
         SFM_LAUNCH(launch_adaln_fp8(x_in, L, 0, L, mod, ms, b.hq, b.hs, B, D, d->eps, st));
-        SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.hq, b.hs, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st, shared));
+        SFM_LAUNCH(launch_attn_pad_zero(b.q, b.k, b.vt, B, L, H, st));
+        const RopeArgs ra = rope_args(ctx, w->q_norm, w->k_norm, b.q, b.k, b.vt, T, gw, L, lens);
+        SFM_TIMED(launch_gemm_fp8_qkv_rope(b.hq, b.hs, (const uint8_t*)w->qkv.q, (const float*)w->qkv.scale, M, D, L,
+                                           ra, st));
     } else {
         SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, mod, ms, b.h, B, D, d->eps, st));
         SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T,
+                                       gh, gw, H, d->eps, lens, st));
     }
-    SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T, gh,
-                                   gw, H, d->eps, lens, st));
     SFM_TIMED(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
     if (fmt == SFM_W_FP8_E4M3) {
@@ -847,6 +872,26 @@ int sfm_qk_norm_rope_varlen(const sfm_context* ctx, const uint16_t* qkv, const u
     for (int i = 0; i < 6; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
     SFM_LAUNCH(launch_qk_norm_rope(qkv, q_norm, k_norm, ctx->rope_cos, ctx->rope_sin, q, k, vt, B, T, gh, gw,
                                    ctx->dims.num_heads, ctx->dims.eps, &lens, (hipStream_t)stream));
+    return SFM_OK;
+}
+
+int sfm_qkv_rope(const sfm_context* ctx, const uint8_t* a, const float* a_scale, const sfm_qweight* w,
+                 const uint16_t* q_norm, const uint16_t* k_norm, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T,
+                 int gh, int gw, const int32_t* text_lens, void* stream) {
+    if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
+    SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
+    const int D = ctx->dims.emb_dim;
+    SFM_CHECK(check_qweight(w, SFM_W_FP8_E4M3, 3 * D, D, "w"));
+    TextLens lens;
+    if (text_lens) SFM_CHECK(make_lens(text_lens, B, T, &lens));
+    const void* ps[] = {a, a_scale, q_norm, k_norm, q, k, vt};
+    const char* ns[] = {"a", "a_scale", "q_norm", "k_norm", "q", "k", "vt"};
+    for (int i = 0; i < 7; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
+    const int L = T + gh * gw;
+    const hipStream_t st = (hipStream_t)stream;
+    SFM_LAUNCH(launch_attn_pad_zero(q, k, vt, B, L, ctx->dims.num_heads, st));
+    const RopeArgs ra = rope_args(ctx, q_norm, k_norm, q, k, vt, T, gw, L, text_lens ? &lens : nullptr);
+    SFM_LAUNCH(launch_gemm_fp8_qkv_rope(a, a_scale, (const uint8_t*)w->q, (const float*)w->scale, B * L, D, L, ra, st));
     return SFM_OK;
 }
 

@@ -129,6 +129,21 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// Rotary position of row l of a sample whose text prefix has T rows, the first Tb of them
+// real text, on one axis (0 t, 1 h, 2 w): text (and padding) rows l -> l on every axis,
+// image token i = l - T at (Tb, Tb + i / gw, Tb + i % gw).
+__device__ __forceinline__ int axis_pos(int l, int T, int Tb, int gw, int axis) {
+    if (l < T) return l;
+    const int i = l - T;
+    if (axis == 0) return Tb;
+    if (axis == 1) return Tb + i / gw;
+    return Tb + i % gw;
+}
+
+// Position of token t (0..31, inside its group of 32) in the attention kernel's V^T rows:
+// the stored order of a group is [4g..4g+3, 16+4g..16+4g+3] for g = 0..3.
+__device__ __forceinline__ int vt_slot(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
+
 #endif  // __HIPCC__
 
 inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -192,6 +207,26 @@ int splitk_parts(int M, int N, int K);
 hipError_t launch_gemm_fp8_splitk(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, uint16_t* out,
                                   int M, int N, int K, float* part, hipStream_t st);
 
+// QKV projection whose epilogue applies QK-RMSNorm (weights qn, kn) and the rotary
+// embedding and writes q, k [B][H][Lp][256] (bf16) and V^T [B][H][256][Lp] (fp16, keys in the
+// stored order of vt_slot) directly, in place of the STORE projection + launch_qk_norm_rope.
+// N = 3 H 256 (q heads, k heads, v heads); rows past each sample's L are not written.
+struct RopeArgs {
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* vt;
+    const uint16_t* qn;
+    const uint16_t* kn;
+    const float* cos_t;
+    const float* sin_t;
+    int T, gw, Lp, H;
+    float eps;
+    int varlen;
+    TextLens lens;
+};
+hipError_t launch_gemm_fp8_qkv_rope(const uint8_t* a, const float* sa, const uint8_t* w, const float* sw, int M,
+                                   int K, int L, const RopeArgs& ra, hipStream_t st);
+
 // k_gemm_nf4.hip
 hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
@@ -202,6 +237,9 @@ hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const f
 hipError_t launch_qk_norm_rope(const uint16_t* qkv, const uint16_t* qn, const uint16_t* kn, const float* cos_t,
                                const float* sin_t, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh,
                                int gw, int H, float eps, const TextLens* lens, hipStream_t st);
+// Zeroes the padding rows [L, Lp) of q and k and the padding columns of V^T (nothing when
+// Lp == L): the attention kernel multiplies V^T's padding by zero weights, so it must be finite.
+hipError_t launch_attn_pad_zero(uint16_t* q, uint16_t* k, uint16_t* vt, int B, int L, int H, hipStream_t st);
 
 // k_attn.hip
 // Attention runs as `grid` persistent workgroups (at most kAttnMaxGrid; one per compute unit)

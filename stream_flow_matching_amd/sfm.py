@@ -89,6 +89,7 @@ SIGNATURES = {
     "sfm_linear": (_I, [_P, _I, _P, _P, ctypes.POINTER(sfm_qweight), _P, _P, _P, _I64, _I, _I, _P]),
     "sfm_padded_len": (_I, [_I]),
     "sfm_qk_norm_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "sfm_qkv_rope": (_I, [_P, _P, _P, ctypes.POINTER(sfm_qweight), _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "sfm_attention": (_I, [_P, _P, _P, _P, _P, _I, _I, _P]),
     "sfm_euler_cfg": (_I, [_P, _P, _P, _P, _P, _I64, _F, _F, _P]),
     "sfm_dequant": (_I, [_P, ctypes.POINTER(sfm_qweight), _P, _I, _P]),
@@ -260,6 +261,19 @@ def sfm_linear(ctx, epilogue, a, a_scale, w: sfm_qweight, out, resid=None, gate=
 def sfm_qk_norm_rope(ctx, qkv, q_norm, k_norm, q, k, vt, B, T, gh, gw, stream=None):
     _check(lib().sfm_qk_norm_rope(ctx.handle, _ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(q), _ptr(k), _ptr(vt), B,
                                   T, gh, gw, _stream(stream)))
+
+
+def sfm_qk_norm_rope_varlen(ctx, qkv, q_norm, k_norm, q, k, vt, B, T, text_lens, gh, gw, stream=None):
+    keep, p = _lens(text_lens)
+    _check(lib().sfm_qk_norm_rope_varlen(ctx.handle, _ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(q), _ptr(k),
+                                         _ptr(vt), B, T, p, gh, gw, _stream(stream)))
+
+
+def sfm_qkv_rope(ctx, a, a_scale, w, q_norm, k_norm, q, k, vt, B, T, gh, gw, text_lens=None, stream=None):
+    """w: an sfm_qweight (FP8, [3D][D]), as made by qweight()."""
+    keep, p = _lens(text_lens) if text_lens is not None else (None, None)
+    _check(lib().sfm_qkv_rope(ctx.handle, _ptr(a), _ptr(a_scale), ctypes.byref(w), _ptr(q_norm), _ptr(k_norm), _ptr(q),
+                              _ptr(k), _ptr(vt), B, T, gh, gw, p, _stream(stream)))
 
 
 def sfm_attention(ctx, q, k, vt, o, B, L, stream=None):
