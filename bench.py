@@ -249,7 +249,7 @@ def text_project_bench(sfm, synth, ctx, M=512, iters=10):
 
 KINDS = ("qkv", "attention", "o", "gate_up", "down")   # a block's matrix launches, in launch order
 KIND_DESC = {
-    "qkv": "gemm_fp8_kernel, STORE epilogue: QKV projection, N 13824, K 4608",
+    "qkv": "gemm_fp8_kernel, QKV projection with QK-RMSNorm + MRoPE in the epilogue (q, k, V^T in the attention layouts), N 13824, K 4608",
     "attention": "attn_kernel on one persistent workgroup per compute unit, with attn_merge_kernel for the "
                  "query blocks split between workgroups (both inside the timed pair): joint attention, 18 heads "
                  "of 256",
@@ -455,7 +455,7 @@ def _step_kinds(rows):
         kind = None
         if n.startswith("gemm_fp8_kernel<"):
             epi = n.split(",")[2].strip()
-            kind = {"0": "qkv", "2": "gate_up", "1": "down" if last == "gate_up" else "o"}.get(epi)
+            kind = {"0": "qkv", "4": "qkv", "2": "gate_up", "1": "down" if last == "gate_up" else "o"}.get(epi)
         elif n.startswith("attn_kernel"):
             kind = "attention"
         if kind:

@@ -107,10 +107,10 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
     float rs[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) rs[i] = rsl[32 * i + lc];
-    // the projection's output values (bf16, the STORE epilogue's rounding) of accumulator
-    // elements (i, j, 4 q .. 4 q + 3)
-    auto y4 = [&](int i, int j, int q) {
-        const v4f cs = *reinterpret_cast<const v4f*>(csl + 32 * j + 8 * q + 4 * lg);
+    // the column scales of a group of four columns; the projection's output values (bf16, the
+    // STORE epilogue's rounding) of accumulator elements (i, j, 4 q .. 4 q + 3) under them
+    auto colscale = [&](int j, int q) { return *reinterpret_cast<const v4f*>(csl + 32 * j + 8 * q + 4 * lg); };
+    auto y4 = [&](int i, int j, int q, v4f cs) {
         const uint32_t lo = cvt_bf16x2(acc[i][j][4 * q] * rs[i] * cs[0], acc[i][j][4 * q + 1] * rs[i] * cs[1]);
         const uint32_t hi = cvt_bf16x2(acc[i][j][4 * q + 2] * rs[i] * cs[2], acc[i][j][4 * q + 3] * rs[i] * cs[3]);
         return v4f{__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u), __uint_as_float(hi << 16),
@@ -119,35 +119,43 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
     // the wave's rows span at most two samples (L >= 256 > TM)
     const int b_first = min(m0w, M - 1) / L, split = (b_first + 1) * L;
     if (part < 2) {
-        float rn[FM];
+        float rn[FM] = {};
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f cs = colscale(j, q);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const v4f u = y4(i, j, q, cs);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rn[i] += u[e] * u[e];
+                }
+            }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            float ss = 0.f;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4f u = y4(i, j, q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
-                }
-            ss += __shfl_xor(ss, 32, 64);
-            rn[i] = ss;
-            if (lg == 0) xch[(2 * wm + wn) * TM + 32 * i + lc] = ss;
+            rn[i] += __shfl_xor(rn[i], 32, 64);
+            if (lg == 0) xch[(2 * wm + wn) * TM + 32 * i + lc] = rn[i];
         }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             rn[i] = 1.0f / sqrtf((rn[i] + xch[(2 * wm + (wn ^ 1)) * TM + 32 * i + lc]) / 256.0f + ra.eps);
-        // the norm weights of the lane's 64 columns, loaded once (bf16 pairs)
+        // the rows' positions on the three axes (wave 0 rotates)
+        int pax[FM][3];
+        if (wn == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = min(m0w + 32 * i + lc, M - 1);
+                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
+                const int Tb = ra.varlen ? ra.lens.len[b] : ra.T;
+#pragma unroll
+                for (int a = 0; a < 3; ++a) pax[i][a] = axis_pos(l, ra.T, Tb, ra.gw, a);
+            }
+        }
         const uint16_t* gam = (part == 0 ? ra.qn : ra.kn) + wn * TN;
-        uint2 gw[FN][4];
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) gw[j][q] = *reinterpret_cast<const uint2*>(gam + 32 * j + 8 * q + 4 * lg);
         auto gamma4 = [&](int j, int q) {
-            const uint2 g2 = gw[j][q];
+            const uint2 g2 = *reinterpret_cast<const uint2*>(gam + 32 * j + 8 * q + 4 * lg);
             return v4f{__uint_as_float(g2.x << 16), __uint_as_float(g2.x & 0xFFFF0000u), __uint_as_float(g2.y << 16),
                        __uint_as_float(g2.y & 0xFFFF0000u)};
         };
@@ -156,57 +164,52 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
             *reinterpret_cast<uint2*>(lds + row * 256 + ((ch ^ (row & 15)) << 4) + lg * 8) =
                 make_uint2(cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]));
         };
+        // wave 0: cos / sin of the four rows for column group g = 4 j + q (pairs p0 .. p0 + 3, which
+        // share an axis: the section boundaries 24 and 44 are multiples of 4), one group ahead
+        v4f c2[2][FM], s2[2][FM];
+        auto load_cs = [&](int slot, int g) {
+            const int p0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * lg;
+            const int ax = p0 < 24 ? 0 : (p0 < 44 ? 1 : 2);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = 32 * i + lc;
-            // wave 0: the cos / sin of the row's 32 pairs p0 .. p0 + 3 (p0 = 32 j + 8 q + 4 lg), all
-            // loads issued before any is used; four pairs share an axis (the section boundaries
-            // 24 and 44 are multiples of 4)
-            v4f cs4[FN / 2][4], sn4[FN / 2][4];
-            if (wn == 0) {
-                const int m = min(m0w + row, M - 1);
-                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
-                const int Tb = ra.varlen ? ra.lens.len[b] : ra.T;
-                const int pt = axis_pos(l, ra.T, Tb, ra.gw, 0), ph = axis_pos(l, ra.T, Tb, ra.gw, 1),
-                          pw = axis_pos(l, ra.T, Tb, ra.gw, 2);
-#pragma unroll
-                for (int j = 0; j < FN / 2; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int p0 = 32 * j + 8 * q + 4 * lg;
-                        const int pos = p0 < 24 ? pt : (p0 < 44 ? ph : pw);
-                        cs4[j][q] = *reinterpret_cast<const v4f*>(ra.cos_t + pos * 64 + p0);
-                        sn4[j][q] = *reinterpret_cast<const v4f*>(ra.sin_t + pos * 64 + p0);
-                    }
+            for (int i = 0; i < FM; ++i) {
+                c2[slot][i] = *reinterpret_cast<const v4f*>(ra.cos_t + pax[i][ax] * 64 + p0);
+                s2[slot][i] = *reinterpret_cast<const v4f*>(ra.sin_t + pax[i][ax] * 64 + p0);
             }
+        };
+        if (wn == 0) load_cs(0, 0);
 #pragma unroll
-            for (int j = 0; j < FN / 2; ++j)
+        for (int j = 0; j < FN / 2; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // columns c (fragment column j) and c + 64 (fragment column j + 2)
-                    const v4f ga = gamma4(j, q), gb = gamma4(j + FN / 2, q);
-                    v4f a = y4(i, j, q), bb = y4(i, j + FN / 2, q);
+            for (int q = 0; q < 4; ++q) {
+                // columns c (fragment column j) and c + 64 (fragment column j + 2)
+                const int g = 4 * j + q;
+                if (wn == 0 && g + 1 < 2 * FN) load_cs((g + 1) & 1, g + 1);
+                const v4f csa = colscale(j, q), csb = colscale(j + FN / 2, q);
+                const v4f ga = gamma4(j, q), gb = gamma4(j + FN / 2, q);
+                const v4f* c = c2[g & 1];
+                const v4f* sn = s2[g & 1];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    v4f a = y4(i, j, q, csa), bb = y4(i, j + FN / 2, q, csb);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         a[e] = a[e] * rn[i] * ga[e];
                         bb[e] = bb[e] * rn[i] * gb[e];
                     }
                     if (wn == 0) {
-                        // rotation of pairs p0 .. p0 + 3 (dims c, c + 64)
-                        const v4f c = cs4[j][q], sn = sn4[j][q];
                         v4f ra4, rb4;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            ra4[e] = a[e] * c[e] - bb[e] * sn[e];
-                            rb4[e] = bb[e] * c[e] + a[e] * sn[e];
+                            ra4[e] = a[e] * c[i][e] - bb[e] * sn[i][e];
+                            rb4[e] = bb[e] * c[i][e] + a[e] * sn[i][e];
                         }
                         a = ra4;
                         bb = rb4;
                     }
-                    stage(row, 4 * j + q, a);
-                    stage(row, 4 * (j + FN / 2) + q, bb);
+                    stage(32 * i + lc, 4 * j + q, a);
+                    stage(32 * i + lc, 4 * (j + FN / 2) + q, bb);
                 }
-        }
+            }
         uint16_t* const dst = part == 0 ? ra.q : ra.k;
 #pragma unroll
         for (int s = 0; s < TM * 16 / 64; ++s) {
@@ -226,12 +229,13 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
             // c ^ ((d >> 2) & 15); the lane's token 32 i + lc sits at 32 i + vt_slot(lc)
             const int sl = vt_slot(lc);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int q = 0; q < 4; ++q) {
+                    const v4f cs = colscale(j, q);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v4f u = y4(i, j, q);
+                    for (int i = 0; i < FM; ++i) {
+                        const v4f u = y4(i, j, q, cs);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int d = 32 * j + 8 * q + 4 * lg + e, t = 32 * i + sl;
@@ -239,6 +243,7 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
                                                          (t & 7) * 2) = f16(u[e]);
                         }
                     }
+                }
             uint16_t* const vt = ra.vt + ((int64_t)b_first * ra.H + h) * 256 * ra.Lp;
 #pragma unroll
             for (int s = 0; s < TN * 16 / 64; ++s) {
@@ -258,7 +263,7 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const v4f u = y4(i, j, q);
+                        const v4f u = y4(i, j, q, colscale(j, q));
 #pragma unroll
                         for (int e = 0; e < 4; ++e) base[(int64_t)(32 * j + 8 * q + 4 * lg + e) * ra.Lp] = f16(u[e]);
                     }
