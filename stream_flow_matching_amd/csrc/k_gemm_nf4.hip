@@ -13,8 +13,10 @@
 // goes global -> LDS with buffer_load ... lds; the weight tile is decoded by the
 // workgroup itself: each thread owns one weight row (two threads per row for
 // BN = 128), loads its 32 (16) packed bytes and the block's absmax a stage
-// ahead, looks the 4-bit codes up in a 16-entry fp32 codebook in LDS,
-// multiplies by the absmax and rounds to bf16 into the stage.  Each stage is
+// ahead, looks each packed byte up in a 256-entry table of codebook value
+// pairs in LDS (one 8-byte read for two weights), multiplies by the absmax
+// and rounds to bf16 into the stage; the lookups and the scaling are issued
+// a few matrix-core instructions apart so the reads' latency is hidden.  Each stage is
 // four 16-k substeps of v_mfma_f32_32x32x16_bf16 with the next substep's
 // fragments read during the current one; the decode of the next stage is
 // spread over the substeps so that its VALU work runs beside the matrix cores.
@@ -89,9 +91,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int STAGE = (BM + BN) * kRowB;
     static_assert(TPR * BN == 256 && EPP % 8 == 0, "decode ownership");
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds_base[];
-    // the codebook sits at LDS offset 0 (a lookup address is just 4 q), the ring after it
-    float* lut = reinterpret_cast<float*>(lds_base);
-    uint8_t* const smem = lds_base + 1024;
+    // the codebook of byte pairs sits at LDS offset 0 (a lookup address is just 8 b for the packed
+    // byte b: its two elements' values side by side), the ring after it
+    float2* lut2 = reinterpret_cast<float2*>(lds_base);
+    uint8_t* const smem = lds_base + 2048;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     grouped_tile(xcd_tile_id(), ntm, ntn, kGroupM, tm, tn);
     const int m0 = tm * BM;
     const int nks = K / kBK;
-    if (tid < 16) lut[tid] = code.v[tid];
+    lut2[tid] = make_float2(code.v[tid >> 4], code.v[tid & 15]);  // high nibble: the earlier element
     // the epilogue's factors go to LDS behind the ring: row and column scales (1: bf16 operands)
     // and, for the gated residual, the gate rows of the (at most three) batches the tile's rows
     // touch; written here, read after the main loop's barriers
@@ -150,21 +153,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         am[slot] = asrc[s];
     };
-    // part p: weights eo + EPP p .. + EPP - 1 -> EPP / 8 swizzled 16-byte chunks of row br
-    auto decode = [&](int slot, uint8_t* stg, int p) {
+    // part p: weights eo + EPP p .. + EPP - 1 -> EPP / 8 swizzled 16-byte chunks of row br, in two
+    // halves that the main loop places apart: the codebook lookups (one per packed byte), then the
+    // scaling, rounding and stores, so that the lookups' latency runs under matrix-core work
+    float2 cvp[EPP / 2];
+    auto lookup = [&](int slot, int p) {
 #pragma unroll
         for (int c = 0; c < EPP / 8; ++c) {
             const uint32_t w = nb[slot][p * (EPP / 8) + c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cvp[4 * c + e] = lut2[__builtin_amdgcn_ubfe(w, 8 * e, 8)];
+        }
+    };
+    auto finish = [&](int slot, uint8_t* stg, int p) {
+#pragma unroll
+        for (int c = 0; c < EPP / 8; ++c) {
             uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t hi = __builtin_amdgcn_ubfe(w, 8 * e + 4, 4);  // element 2i
-                const uint32_t lo = __builtin_amdgcn_ubfe(w, 8 * e, 4);      // element 2i + 1
-                o[e] = cvt_bf16x2(lut[hi] * am[slot], lut[lo] * am[slot]);
-            }
+            for (int e = 0; e < 4; ++e) o[e] = cvt_bf16x2(cvp[4 * c + e].x * am[slot], cvp[4 * c + e].y * am[slot]);
             const int lc = (eo + EPP * p) / 8 + c;
             *reinterpret_cast<u32x4*>(stg + BM * kRowB + br * kRowB + ((lc ^ bsx) << 4)) = u32x4{o[0], o[1], o[2], o[3]};
         }
+    };
+    auto decode = [&](int slot, uint8_t* stg, int p) {
+        lookup(slot, p);
+        finish(slot, stg, p);
     };
     auto dma = [&](int v, uint8_t* stg, __amdgpu_buffer_rsrc_t r, int s) {
         dma16(r, stg + wave * 1024 + v * 4096, voff[v], s * (kBK * 2));
@@ -203,7 +216,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (RD)
 #pragma unroll
                 for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) ds(rset, f, rstg, rks);
-            if (DEC && q == NQ / 2) decode(dslot, dstg, dp);
+            if (DEC && q == NQ / 8) lookup(dslot, dp);
+            if (DEC && q == NQ / 2 + NQ / 8) finish(dslot, dstg, dp);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -263,7 +277,7 @@ hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, cons
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 1024 + (size_t)(BM + 4 * BN) * 4;
+    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 2048 + (size_t)(BM + 4 * BN) * 4;
     auto kern = gemm_nf4_kernel<BM, BN, EPI>;
     static std::atomic<uint64_t> lds_raised{0};
     raise_lds_limit_once((const void*)kern, shm, lds_raised);
