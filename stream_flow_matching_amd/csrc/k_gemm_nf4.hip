@@ -88,13 +88,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int TPR = kBK / EPT;             // threads per weight row
     constexpr int EPP = EPT / 4;               // weights per decode part (four parts per stage)
     constexpr int NW = EPT / 8;                // packed dwords per thread per stage
-    constexpr int STAGE = (BM + BN) * kRowB;
     static_assert(TPR * BN == 256 && EPP % 8 == 0, "decode ownership");
-    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_base[];
-    // the codebook of byte pairs sits at LDS offset 0 (a lookup address is just 8 b for the packed
-    // byte b: its two elements' values side by side), the ring after it
-    float2* lut2 = reinterpret_cast<float2*>(lds_base);
-    uint8_t* const smem = lds_base + 2048;
+    // LDS bytes of one wave's epilogue staging (gemm_epilogue_lds): within the smallest ring array
+    constexpr int EPI_BYTES = EPI == SFM_EPI_RESID_GATE ? TM / 2 * (TN * 4 + ((TN / 4) % 16 ? 16 : 0))
+                                                        : TM * (EPI == SFM_EPI_SWIGLU ? TN / 2 : TN) * 2;
+    static_assert(BN <= BM && EPI_BYTES <= BN * kRowB, "epilogue staging fits a ring array");
+    // LDS: the two-stage ring as four separate arrays (activation and weight half of each stage),
+    // the codebook of byte pairs (entry b: the values of packed byte b's two elements side by side)
+    // and the epilogue's factors.  Distinct arrays let the compiler see that the codebook reads and
+    // the decoded-weight writes do not touch the activation halves that the direct global -> LDS
+    // loads fill, so it does not make them wait for those loads.
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_a0[BM * kRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_a1[BM * kRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_b0[BN * kRowB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring_b1[BN * kRowB];
+    __shared__ float2 lut2[256];
+    __shared__ float scl_lds[BM + 4 * BN];
+    auto stage_a = [&](int s) -> uint8_t* { return s ? ring_a1 : ring_a0; };
+    auto stage_b = [&](int s) -> uint8_t* { return s ? ring_b1 : ring_b0; };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,10 +115,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int m0 = tm * BM;
     const int nks = K / kBK;
     lut2[tid] = make_float2(code.v[tid >> 4], code.v[tid & 15]);  // high nibble: the earlier element
-    // the epilogue's factors go to LDS behind the ring: row and column scales (1: bf16 operands)
-    // and, for the gated residual, the gate rows of the (at most three) batches the tile's rows
-    // touch; written here, read after the main loop's barriers
-    float* scl = reinterpret_cast<float*>(smem + 2 * STAGE);
+    // the epilogue's factors: row and column scales (1: bf16 operands) and, for the gated
+    // residual, the gate rows of the (at most three) batches the tile's rows touch; written here,
+    // read after the main loop's barriers
+    float* scl = scl_lds;
     const int bt0 = EPI == SFM_EPI_RESID_GATE ? min(m0, M - 1) / L : 0;
     for (int e = tid; e < BM + (EPI == SFM_EPI_RESID_GATE ? 4 : 1) * BN; e += 256) {
         float v = 1.0f;
@@ -153,34 +164,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         am[slot] = asrc[s];
     };
-    // part p: weights eo + EPP p .. + EPP - 1 -> EPP / 8 swizzled 16-byte chunks of row br, in two
-    // halves that the main loop places apart: the codebook lookups (one per packed byte), then the
-    // scaling, rounding and stores, so that the lookups' latency runs under matrix-core work
+    // part p: weights eo + EPP p .. + EPP - 1 -> EPP / 8 swizzled 16-byte chunks of row br of the
+    // weight half of stage stg.  The main loop spreads it over the matrix-core instructions in
+    // pieces: the codebook lookups of chunk c (one per packed byte), and later the scaling and
+    // rounding of half a chunk (piece k: chunk k >> 1, elements 4 (k & 1) .. +3), the chunk's
+    // 16-byte store after its second half
     float2 cvp[EPP / 2];
-    auto lookup = [&](int slot, int p) {
+    uint32_t ob[EPP / 8][4];
+    auto lookup_c = [&](int slot, int p, int c) {
+        const uint32_t w = nb[slot][p * (EPP / 8) + c];
 #pragma unroll
-        for (int c = 0; c < EPP / 8; ++c) {
-            const uint32_t w = nb[slot][p * (EPP / 8) + c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cvp[4 * c + e] = lut2[__builtin_amdgcn_ubfe(w, 8 * e, 8)];
-        }
+        for (int e = 0; e < 4; ++e) cvp[4 * c + e] = lut2[__builtin_amdgcn_ubfe(w, 8 * e, 8)];
     };
-    auto finish = [&](int slot, uint8_t* stg, int p) {
+    auto finish_k = [&](int slot, int stg, int p, int k) {
+        const int c = k >> 1, h = k & 1;
 #pragma unroll
-        for (int c = 0; c < EPP / 8; ++c) {
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = cvt_bf16x2(cvp[4 * c + e].x * am[slot], cvp[4 * c + e].y * am[slot]);
+        for (int e = 2 * h; e < 2 * h + 2; ++e)
+            ob[c][e] = cvt_bf16x2(cvp[4 * c + e].x * am[slot], cvp[4 * c + e].y * am[slot]);
+        if (h) {
             const int lc = (eo + EPP * p) / 8 + c;
-            *reinterpret_cast<u32x4*>(stg + BM * kRowB + br * kRowB + ((lc ^ bsx) << 4)) = u32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4*>(stage_b(stg) + br * kRowB + ((lc ^ bsx) << 4)) =
+                u32x4{ob[c][0], ob[c][1], ob[c][2], ob[c][3]};
         }
     };
-    auto decode = [&](int slot, uint8_t* stg, int p) {
-        lookup(slot, p);
-        finish(slot, stg, p);
+    auto decode = [&](int slot, int stg, int p) {
+#pragma unroll
+        for (int c = 0; c < EPP / 8; ++c) lookup_c(slot, p, c);
+#pragma unroll
+        for (int k = 0; k < EPP / 4; ++k) finish_k(slot, stg, p, k);
     };
-    auto dma = [&](int v, uint8_t* stg, __amdgpu_buffer_rsrc_t r, int s) {
-        dma16(r, stg + wave * 1024 + v * 4096, voff[v], s * (kBK * 2));
+    auto dma = [&](int v, int stg, __amdgpu_buffer_rsrc_t r, int s) {
+        dma16(r, stage_a(stg) + wave * 1024 + v * 4096, voff[v], s * (kBK * 2));
     };
 
     v16f acc[FM][FN];
@@ -191,11 +205,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // fragments: lane l holds row (l & 31) and 16-byte chunk 2 ks + (l >> 5) of substep ks
     const int lr = lane & 31, lg = lane >> 5, sx = (lr >> 1) & 7;
-    const int arow = (wm * TM + lr) * kRowB, brow = BM * kRowB + (wn * TN + lr) * kRowB;
+    const int arow = (wm * TM + lr) * kRowB, brow = (wn * TN + lr) * kRowB;
     u32x4 fr[2][NF];  // f < FN: weight column tile f, else row tile f - FN
-    auto ds = [&](int set, int f, const uint8_t* stg, int ks) {
+    auto ds = [&](int set, int f, int stg, int ks) {
         const int off = ((2 * ks + lg) ^ sx) << 4;
-        fr[set][f] = *reinterpret_cast<const u32x4*>(stg + (f < FN ? brow + f * 32 * kRowB : arow + (f - FN) * 32 * kRowB) + off);
+        fr[set][f] = *reinterpret_cast<const u32x4*>(f < FN ? stage_b(stg) + brow + f * 32 * kRowB + off
+                                                            : stage_a(stg) + arow + (f - FN) * 32 * kRowB + off);
     };
     auto mfma = [&](int set, int q) {
         const int i = q / FN, j = q % FN;
@@ -204,8 +219,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // substep: FM x FN MFMAs on `set`, with spread over them: the fragment reads of (rstg, rks)
     // into rset (if RD), decode part dp of `dslot` into dstg (if DEC), wave-loads v0 .. v1 (if DM)
-    auto substep = [&](int set, bool RD, int rset, const uint8_t* rstg, int rks, bool DEC, int dslot, uint8_t* dstg,
-                       int dp, bool DM, uint8_t* mstg, __amdgpu_buffer_rsrc_t mr, int ms) {
+    auto substep = [&](int set, bool RD, int rset, int rstg, int rks, bool DEC, int dslot, int dstg, int dp,
+                       bool DM, int mstg, __amdgpu_buffer_rsrc_t mr, int ms) {
         constexpr int NQ = FM * FN;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -216,8 +231,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (RD)
 #pragma unroll
                 for (int f = q * NF / NQ; f < (q + 1) * NF / NQ; ++f) ds(rset, f, rstg, rks);
-            if (DEC && q == NQ / 8) lookup(dslot, dp);
-            if (DEC && q == NQ / 2 + NQ / 8) finish(dslot, dstg, dp);
+            if (DEC && q >= 1 && q < 1 + EPP / 8) lookup_c(dslot, dp, q - 1);
+            if (DEC && q >= NQ / 2 && q < NQ / 2 + EPP / 4) finish_k(dslot, dstg, dp, q - NQ / 2);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -227,18 +242,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     nib_load(0, 0);
     nib_load(1, 1);
 #pragma unroll
-    for (int v = 0; v < AI; ++v) dma(v, smem, ra, 0);
+    for (int v = 0; v < AI; ++v) dma(v, 0, ra, 0);
 #pragma unroll
-    for (int v = 0; v < AI; ++v) dma(v, smem + STAGE, ra, 1);
+    for (int v = 0; v < AI; ++v) dma(v, 1, ra, 1);
     wait_vm_lgkm0<0>();
     lds_barrier();
 #pragma unroll
-    for (int p = 0; p < 4; ++p) decode(0, smem, p);
-    decode(1, smem + STAGE, 0);
+    for (int p = 0; p < 4; ++p) decode(0, 0, p);
+    decode(1, 1, 0);
     wait_vm_lgkm0<0>();
     lds_barrier();
 #pragma unroll
-    for (int f = 0; f < NF; ++f) ds(0, f, smem, 0);
+    for (int f = 0; f < NF; ++f) ds(0, f, 0, 0);
 
     // stage t: set 0 holds substep 0 of stage t on entry and substep 0 of stage t + 1 on exit;
     // weights of stage t + 1 are decoded in parts 1..3 here (part 0 in stage t - 1), those
@@ -247,8 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the two register slots of packed weights alternate with the stage's parity (compile-time)
     auto stage = [&](auto P, int t) {
         constexpr int s2 = decltype(P)::value, s1 = s2 ^ 1;  // slots of stages t + 2 and t + 1
-        uint8_t* cur = smem + s2 * STAGE;
-        uint8_t* nxt = smem + s1 * STAGE;
+        constexpr int cur = s2, nxt = s1;                      // ring stages of t (and t + 2), t + 1
         const __amdgpu_buffer_rsrc_t rA = t + 2 < nks ? ra : ra0;
         substep(0, true, 1, cur, 1, true, s1, nxt, 1, false, cur, rA, 0);
         nib_load(s2, t + 2);
@@ -267,7 +281,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     wait_vm_lgkm0<0>();
     lds_barrier();
-    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (STAGE / 2), m0 + wm * TM, wn, tn, lane, M, N, L, out,
+    // each wave stages its tile through one of the four ring arrays
+    uint8_t* const estg = wave == 0 ? ring_a0 : wave == 1 ? ring_b0 : wave == 2 ? ring_a1 : ring_b1;
+    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, estg, m0 + wm * TM, wn, tn, lane, M, N, L, out,
                                              resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
 }
 
@@ -277,11 +293,8 @@ hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, cons
                       hipStream_t st) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
-    const size_t shm = (size_t)2 * (BM + BN) * kRowB + 2048 + (size_t)(BM + 4 * BN) * 4;
-    auto kern = gemm_nf4_kernel<BM, BN, EPI>;
-    static std::atomic<uint64_t> lds_raised{0};
-    raise_lds_limit_once((const void*)kern, shm, lds_raised);
-    hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), shm, st, a, w, am, code, out, resid, gate, gate_stride, M, N,
+    auto kern = gemm_nf4_kernel<BM, BN, EPI>;  // all of its LDS is static
+    hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), 0, st, a, w, am, code, out, resid, gate, gate_stride, M, N,
                        K, L, ntm, ntn);
     return hipGetLastError();
 }
