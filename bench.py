@@ -56,6 +56,12 @@ def parse():
                     help="time the vendor libraries at this path's shapes (hipBLASLt FP8 through torch._scaled_mm, "
                          "bf16 torch.mm, torch's scaled_dot_product_attention) and exit; a context figure, not part "
                          "of the path")
+    ap.add_argument("--block-probe", metavar="WORKLOAD",
+                    help="run only a few forwards of one block of a named workload (e.g. block_6to1_nf4) and a "
+                         "calibration copy (for rocprofv3 kernel-trace and --pmc passes) and exit")
+    ap.add_argument("--block-summary", nargs="+", metavar="DIR",
+                    help="per-kernel table (markdown) of the block_6to1_nf4 matrix launches from rocprofv3 output "
+                         "directories of --block-probe (a kernel trace and/or --pmc passes) and exit (no GPU needed)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="print per-kernel tables (markdown) from a rocprofv3 --kernel-trace --stats output "
                          "directory of this script and exit (no GPU needed)")
@@ -430,6 +436,137 @@ def pmc_probe(sfm, synth, ctx):
                       "sources_sha256_16": {k: sources_digest(k) for k in KINDS}}))
 
 
+BLOCK_PROBE_CALLS = 4   # block forwards run by --block-probe (the first one warms up)
+
+
+def block_probe(sfm, synth, ctx, name):
+    """For rocprofv3 runs: BLOCK_PROBE_CALLS forwards of one block of workload `name`
+    (weights drawn on the device), then a plain device copy of COPY_BYTES that
+    calibrates the byte counters."""
+    import torch
+    w = synth.WORKLOADS[name]
+    p = synth.block_params(w.shape, (0, w.name), w.wfmt, device="cuda")
+    bw = sfm.BlockWeights(p)
+    x, c = synth.block_inputs(w, device="cuda")
+    xo = torch.empty_like(x)
+    ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx, w.B, w.T, w.gh, w.gw, bw.fmt))
+    ms = []
+    for _ in range(BLOCK_PROBE_CALLS):
+        ms.append(time_gpu(lambda: sfm.sfm_block_forward(ctx, bw, x, xo, c, w.B, w.T, w.gh, w.gw, ws), 1, 0) * 1e3)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"block_probe": name, "weights": w.wfmt, "ms": [round(v, 3) for v in ms],
+                      "copy_bytes": COPY_BYTES}))
+
+
+def block_work(kind, M, wfmt, D=4608, F=12288):
+    """(algorithmic FLOP, algorithmic HBM bytes) of one projection of a block with M token
+    rows.  NF4 weights: bf16 activation in, packed nibbles + fp32 absmax per 64 weights,
+    bf16 out (+ the bf16 residual read for the gated residual); FP8 as kernel_work."""
+    if wfmt != "nf4":
+        return kernel_work(kind, M)
+    n, k = {"qkv": (3 * D, D), "o": (D, D), "gate_up": (2 * F, D), "down": (D, F)}[kind]
+    out_cols = n // 2 if kind == "gate_up" else n
+    nbytes = 2 * M * k + n * k // 2 + 4 * (n * k // 64) + 2 * M * out_cols + (2 * M * n if kind in ("o", "down") else 0)
+    return 2.0 * M * n * k, nbytes
+
+
+def _block_kinds(order):
+    """Label the matrix launches of block forwards (dispatches in launch order): QKV,
+    attention, O, gate/up, down; the first forward (the warm-up) is left out."""
+    labels, last, n = {}, None, 0
+    for r in order:
+        k = _short(r["Kernel_Name"])
+        kind = None
+        if k.startswith("gemm_fp8_kernel<") or k.startswith("gemm_nf4_kernel<"):
+            epi = k.split(",")[2].strip().rstrip(">")
+            kind = {"0": "qkv", "4": "qkv", "2": "gate_up", "1": "down" if last == "gate_up" else "o"}.get(epi)
+        elif k.startswith("attn_kernel"):
+            kind = "attention"
+        if kind:
+            n += kind == "qkv"
+            if n > 1:
+                labels[r["Dispatch_Id"]] = kind
+            last = kind
+    return labels
+
+
+def block_summary(dirs, name="block_6to1_nf4"):
+    """Markdown table from rocprofv3 runs over --block-probe: per matrix launch kind of the
+    block, durations from a kernel trace and counters averaged per dispatch from --pmc
+    passes; FETCH_SIZE / WRITE_SIZE scaled by what they read for the calibration copy."""
+    import csv
+    import glob
+    from collections import defaultdict
+    from stream_flow_matching_amd import synth
+    w = synth.WORKLOADS[name]
+    M = w.B * w.L
+    dur = defaultdict(list)
+    vals = defaultdict(lambda: defaultdict(list))
+    copy = defaultdict(list)
+    names = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"]))
+            for r in rows:
+                r["Dispatch_Id"] = r.get("Dispatch_Id") or r["Correlation_Id"]
+            lab = _block_kinds(rows)
+            for r in rows:
+                if r["Dispatch_Id"] in lab:
+                    dur[lab[r["Dispatch_Id"]]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                    names[lab[r["Dispatch_Id"]]] = _short(r["Kernel_Name"])
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(f)))
+            disp = {}
+            for r in rows:
+                disp.setdefault(r["Dispatch_Id"], r)
+            lab = _block_kinds(sorted(disp.values(), key=lambda r: int(r["Dispatch_Id"])))
+            for r in rows:
+                if r["Dispatch_Id"] in lab:
+                    vals[lab[r["Dispatch_Id"]]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                    names[lab[r["Dispatch_Id"]]] = _short(r["Kernel_Name"])
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    copy[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    mean = lambda v: sum(v) / len(v)
+    scale = {c: COPY_BYTES / (mean(v) * 1024) for c, v in copy.items() if c in ("FETCH_SIZE", "WRITE_SIZE") and v}
+    peak = BF16_PEAK_TFLOPS if w.wfmt == "nf4" else FP8_PEAK_TFLOPS
+    print(f"Workload {name}: {w.describe}; M = {M} token rows; weights {w.wfmt}.")
+    print()
+    print("| kind | kernel | launches | avg us | TFLOP/s | % of matrix peak | MfmaUtil (%) "
+          "| LDS conflict cycles / active | FETCH + WRITE (MB, scaled) | algorithmic (MB) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for kind in KINDS:
+        if kind not in names:
+            continue
+        if kind == "attention":
+            fl, ab = 4.0 * w.B * w.L * w.L * 4608, 8 * M * 4608
+        else:
+            fl, ab = block_work(kind, M, w.wfmt)
+        us = mean(dur[kind]) if dur.get(kind) else None
+        pk = BF16_PEAK_TFLOPS if kind == "attention" else peak
+        tf = f"{fl / us / 1e6:.1f}" if us else ""
+        frac = f"{100 * fl / us / 1e6 / pk:.1f}" if us else ""
+        cv = vals.get(kind, {})
+        util = f"{mean(cv['MfmaUtil']):.1f}" if "MfmaUtil" in cv else ""
+        conf = ""
+        if "SQ_LDS_BANK_CONFLICT" in cv and "SQ_LDS_IDX_ACTIVE" in cv and mean(cv["SQ_LDS_IDX_ACTIVE"]) > 0:
+            conf = f"{mean(cv['SQ_LDS_BANK_CONFLICT']) / mean(cv['SQ_LDS_IDX_ACTIVE']):.3f}"
+        traffic = ""
+        if "FETCH_SIZE" in cv and "WRITE_SIZE" in cv and "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+            tb = (mean(cv["FETCH_SIZE"]) * scale["FETCH_SIZE"] + mean(cv["WRITE_SIZE"]) * scale["WRITE_SIZE"]) * 1024
+            traffic = f"{tb / 1e6:.1f}"
+        n = len(dur.get(kind, [])) or max((len(v) for v in cv.values()), default=0)
+        avg = f"{us:.1f}" if us else ""
+        print(f"| {kind} | `{names[kind]}` | {n} | {avg} | {tf} | {frac} | {util} | {conf} | {traffic} "
+              f"| {ab / 1e6:.1f} |")
+    if scale:
+        print()
+        print("Byte-counter scales from the copy of %d MiB: %s." % (COPY_BYTES >> 20, ", ".join(
+            f"{c} x {v:.4f} KiB -> bytes" for c, v in sorted(scale.items()))))
+
+
 def _short(n):
     n = n.replace("sfm::(anonymous namespace)::", "").replace("sfm::", "")
     n = n[5:] if n.startswith("void ") else n
@@ -718,6 +855,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
         return
+    if args.block_summary:
+        block_summary(args.block_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -734,6 +874,9 @@ def main():
     ctx = sfm.Context("ideogram4", 0)
     if args.pmc_probe:
         pmc_probe(sfm, synth, ctx)
+        return
+    if args.block_probe:
+        block_probe(sfm, synth, ctx, args.block_probe)
         return
 
     w = synth.WORKLOADS["cfg_step_1024"]
