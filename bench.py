@@ -263,8 +263,8 @@ KIND_DESC = {
     "gate_up": "gemm_fp8_kernel, SwiGLU epilogue: gate/up projection, N 24576, K 4608",
     "down": "gemm_fp8_kernel, gated-residual epilogue: down projection, N 4608, K 12288",
 }
-KIND_SOURCES = {k: ("stream_flow_matching_amd/csrc/k_gemm_fp8.hip", "stream_flow_matching_amd/csrc/gemm_common.h")
-                for k in KINDS}
+KIND_SOURCES = {k: ("stream_flow_matching_amd/csrc/k_gemm_fp8.hip", "stream_flow_matching_amd/csrc/gemm_common.h",
+                    "stream_flow_matching_amd/csrc/epi_qkv_rope.h") for k in KINDS}
 KIND_SOURCES["attention"] = ("stream_flow_matching_amd/csrc/k_attn.hip",)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "cfg_step_1024_counters.md")
 COPY_BYTES = 256 << 20            # plain copy kernel used to calibrate the byte counters

@@ -214,10 +214,10 @@ int sfm_padded_len(int L);
 int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t* q_norm, const uint16_t* k_norm,
                      uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T, int gh, int gw, void* stream);
 
-/* The QKV projection and sfm_qk_norm_rope in one kernel: the FP8 projection of
- * a (E4M3 codes [B*L][D], row scales a_scale [B*L]) by w (FP8, [3D][D]: q,
- * k, v heads of 256), each output rounded to bf16 as sfm_linear's STORE
- * epilogue would, then QK-RMSNorm with q_norm / k_norm and the 3-D MRoPE
+/* The QKV projection and sfm_qk_norm_rope in one kernel: the projection of a
+ * by w ([3D][D]: q, k, v heads of 256), each output rounded to bf16 as
+ * sfm_linear's STORE epilogue would, then QK-RMSNorm with q_norm / k_norm and
+ * the 3-D MRoPE
  * exactly as sfm_qk_norm_rope defines them (research note block internals),
  * written straight to q, k [B][H][Lp][256] (bf16) and vt [B][H][256][Lp]
  * (fp16, sfm_qk_norm_rope's stored key order); padding rows / columns are
@@ -225,9 +225,12 @@ int sfm_qk_norm_rope(const sfm_context* ctx, const uint16_t* qkv, const uint16_t
  * [0, T] (the positions of sfm_qk_norm_rope_varlen), or NULL when every sample
  * has T.  The row's sum of squares adds in another order than the separate
  * kernel's, so q and k can differ from sfm_linear + sfm_qk_norm_rope in the
- * last bf16 place; v is the same bit for bit.  Errors as sfm_linear and
- * sfm_qk_norm_rope (w must be FP8 with n = 3 emb_dim, k = emb_dim). */
-int sfm_qkv_rope(const sfm_context* ctx, const uint8_t* a, const float* a_scale, const sfm_qweight* w,
+ * last bf16 place; v is the same bit for bit.  Weight formats: FP8 (a: E4M3
+ * codes [B*L][D] with row scales a_scale [B*L]) or NF4 block 64 (deployment
+ * post, section 2.1: a is bf16 [B*L][D], a_scale is ignored and may be NULL).
+ * Errors as sfm_linear and sfm_qk_norm_rope (w must be FP8 or NF4 with
+ * n = 3 emb_dim, k = emb_dim). */
+int sfm_qkv_rope(const sfm_context* ctx, const void* a, const float* a_scale, const sfm_qweight* w,
                  const uint16_t* q_norm, const uint16_t* k_norm, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T,
                  int gh, int gw, const int32_t* text_lens, void* stream);
 

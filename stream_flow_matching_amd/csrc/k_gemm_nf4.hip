@@ -28,7 +28,7 @@
 // gate rows are loaded into LDS behind the ring at the start.
 #include <type_traits>
 
-#include "gemm_common.h"
+#include "epi_qkv_rope.h"
 
 namespace sfm {
 
@@ -79,7 +79,7 @@ template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_nf4_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wq, const float* __restrict__ absmax, Nf4Code code,
     uint16_t* out, const uint16_t* resid, const float* __restrict__ gate, int64_t gate_stride, int M, int N, int K,
-    int L, int ntm, int ntn) {
+    int L, int ntm, int ntn, RopeArgs rope) {
     constexpr int TM = BM / 2, TN = BN / 2;    // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;  // 32 x 32 MFMA tiles per wave
     constexpr int NF = FM + FN;                // fragments per substep
@@ -283,19 +283,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     lds_barrier();
     // each wave stages its tile through one of the four ring arrays
     uint8_t* const estg = wave == 0 ? ring_a0 : wave == 1 ? ring_b0 : wave == 2 ? ring_a1 : ring_b1;
-    gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, estg, m0 + wm * TM, wn, tn, lane, M, N, L, out,
-                                             resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
+    if constexpr (EPI == kEpiQkvRope)
+        epilogue_qkv_rope<FM, FN>(acc, estg, scl + BM + BN, m0 + wm * TM, wm, wn, tn, lane, M, L, scl + wm * TM,
+                                  scl + BM + wn * TN, rope);
+    else
+        gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, estg, m0 + wm * TM, wn, tn, lane, M, N, L, out, resid,
+                                                 scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
 }
 
 template <int BM, int BN, int EPI>
 hipError_t launch_cfg(const uint16_t* a, const uint8_t* w, const float* am, const Nf4Code& code, uint16_t* out,
                       const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N, int K, int L,
-                      hipStream_t st) {
+                      hipStream_t st, const RopeArgs& rope = RopeArgs{}) {
     const int ntm = (M + BM - 1) / BM;
     const int ntn = N / BN;
     auto kern = gemm_nf4_kernel<BM, BN, EPI>;  // all of its LDS is static
     hipLaunchKernelGGL(kern, dim3(ntm * ntn), dim3(256), 0, st, a, w, am, code, out, resid, gate, gate_stride, M, N,
-                       K, L, ntm, ntn);
+                       K, L, ntm, ntn, rope);
     return hipGetLastError();
 }
 
@@ -331,6 +335,13 @@ hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const f
         default:
             return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_nf4_qkv_rope(const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,
+                                    int M, int K, int L, const RopeArgs& ra, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    return launch_cfg<256, 256, kEpiQkvRope>(a, w, absmax, code, nullptr, nullptr, nullptr, 0, M, 3 * ra.H * 256, K, L,
+                                             st, ra);
 }
 
 }  // namespace sfm

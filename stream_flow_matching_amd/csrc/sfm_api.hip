@@ -228,6 +228,12 @@ int check_block_weights(const sfm_dims* d, const sfm_block_weights* w, int* fmt_
     return SFM_OK;
 }
 
+Nf4Code nf4_code(const sfm_context* ctx) {
+    Nf4Code code;
+    memcpy(code.v, ctx->nf4_code, sizeof code.v);
+    return code;
+}
+
 // shared: another pass runs on the GPU at the same time (the FP8 / MXFP4 launchers then pick
 // tiles by efficiency alone)
 hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa, const sfm_qweight* w, uint16_t* out,
@@ -239,10 +245,8 @@ hipError_t gemm(const sfm_context* ctx, int epi, const void* a, const float* sa,
     if (w->fmt == SFM_W_MXFP4)
         return launch_gemm_mx(epi, (const uint8_t*)a, sa, (const uint8_t*)w->q, (const uint8_t*)w->scale, out, resid,
                               gate, gs, M, w->n, w->k, L, st, shared);
-    Nf4Code code;
-    memcpy(code.v, ctx->nf4_code, sizeof code.v);
-    return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, (const float*)w->scale, code, out, resid,
-                           gate, gs, M, w->n, w->k, L, st);
+    return launch_gemm_nf4(epi, (const uint16_t*)a, (const uint8_t*)w->q, (const float*)w->scale, nf4_code(ctx), out,
+                           resid, gate, gs, M, w->n, w->k, L, st);
 }
 
 // Debug mode (sfm_set_sync_check, or SFM_SYNC_CHECK=1 in the environment when the library
@@ -333,10 +337,12 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
         SFM_TIMED(launch_gemm_fp8_qkv_rope(b.hq, b.hs, (const uint8_t*)w->qkv.q, (const float*)w->qkv.scale, M, D, L,
                                            ra, st));
     } else {
+        // NF4: the same fused epilogue on the bf16-operand GEMM
         SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, mod, ms, b.h, B, D, d->eps, st));
-        SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
-        SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T,
-                                       gh, gw, H, d->eps, lens, st));
+        SFM_LAUNCH(launch_attn_pad_zero(b.q, b.k, b.vt, B, L, H, st));
+        const RopeArgs ra = rope_args(ctx, w->q_norm, w->k_norm, b.q, b.k, b.vt, T, gw, L, lens);
+        SFM_TIMED(launch_gemm_nf4_qkv_rope(b.h, (const uint8_t*)w->qkv.q, (const float*)w->qkv.scale, nf4_code(ctx), M, D,
+                                           L, ra, st));
     }
     SFM_TIMED(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
@@ -875,23 +881,31 @@ int sfm_qk_norm_rope_varlen(const sfm_context* ctx, const uint16_t* qkv, const u
     return SFM_OK;
 }
 
-int sfm_qkv_rope(const sfm_context* ctx, const uint8_t* a, const float* a_scale, const sfm_qweight* w,
+int sfm_qkv_rope(const sfm_context* ctx, const void* a, const float* a_scale, const sfm_qweight* w,
                  const uint16_t* q_norm, const uint16_t* k_norm, uint16_t* q, uint16_t* k, uint16_t* vt, int B, int T,
                  int gh, int gw, const int32_t* text_lens, void* stream) {
     if (!ctx) return fail(SFM_E_INVALID_ARG, "ctx is NULL");
     SFM_CHECK(shape_check(&ctx->dims, B, T, gh, gw));
     const int D = ctx->dims.emb_dim;
-    SFM_CHECK(check_qweight(w, SFM_W_FP8_E4M3, 3 * D, D, "w"));
+    if (!w) return fail(SFM_E_INVALID_ARG, "w is NULL");
+    const bool nf4 = w->fmt == SFM_W_NF4_B64;
+    SFM_CHECK(check_qweight(w, nf4 ? SFM_W_NF4_B64 : SFM_W_FP8_E4M3, 3 * D, D, "w"));
     TextLens lens;
     if (text_lens) SFM_CHECK(make_lens(text_lens, B, T, &lens));
-    const void* ps[] = {a, a_scale, q_norm, k_norm, q, k, vt};
-    const char* ns[] = {"a", "a_scale", "q_norm", "k_norm", "q", "k", "vt"};
-    for (int i = 0; i < 7; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
+    const void* ps[] = {a, q_norm, k_norm, q, k, vt};
+    const char* ns[] = {"a", "q_norm", "k_norm", "q", "k", "vt"};
+    for (int i = 0; i < 6; ++i) SFM_CHECK(check_ptr(ps[i], ns[i]));
+    if (!nf4) SFM_CHECK(check_ptr(a_scale, "a_scale"));
     const int L = T + gh * gw;
     const hipStream_t st = (hipStream_t)stream;
     SFM_LAUNCH(launch_attn_pad_zero(q, k, vt, B, L, ctx->dims.num_heads, st));
     const RopeArgs ra = rope_args(ctx, q_norm, k_norm, q, k, vt, T, gw, L, text_lens ? &lens : nullptr);
-    SFM_LAUNCH(launch_gemm_fp8_qkv_rope(a, a_scale, (const uint8_t*)w->q, (const float*)w->scale, B * L, D, L, ra, st));
+    if (nf4)
+        SFM_LAUNCH(launch_gemm_nf4_qkv_rope((const uint16_t*)a, (const uint8_t*)w->q, (const float*)w->scale,
+                                            nf4_code(ctx), B * L, D, L, ra, st));
+    else
+        SFM_LAUNCH(launch_gemm_fp8_qkv_rope((const uint8_t*)a, a_scale, (const uint8_t*)w->q, (const float*)w->scale,
+                                            B * L, D, L, ra, st));
     return SFM_OK;
 }
 

@@ -231,6 +231,10 @@ hipError_t launch_gemm_fp8_qkv_rope(const uint8_t* a, const float* sa, const uin
 hipError_t launch_gemm_nf4(int epi, const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,
                            uint16_t* out, const uint16_t* resid, const float* gate, int64_t gate_stride, int M, int N,
                            int K, int L, hipStream_t st);
+// The NF4 QKV projection (bf16 activation a [M][K]) with the same fused QK-RMSNorm + rotary
+// epilogue and outputs as launch_gemm_fp8_qkv_rope.
+hipError_t launch_gemm_nf4_qkv_rope(const uint16_t* a, const uint8_t* w, const float* absmax, const Nf4Code& code,
+                                    int M, int K, int L, const RopeArgs& ra, hipStream_t st);
 
 // k_rope.hip
 // lens: per-sample text lengths (image positions start at len[b]), or NULL when every sample has T

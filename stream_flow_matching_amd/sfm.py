@@ -270,7 +270,8 @@ def sfm_qk_norm_rope_varlen(ctx, qkv, q_norm, k_norm, q, k, vt, B, T, text_lens,
 
 
 def sfm_qkv_rope(ctx, a, a_scale, w, q_norm, k_norm, q, k, vt, B, T, gh, gw, text_lens=None, stream=None):
-    """w: an sfm_qweight (FP8, [3D][D]), as made by qweight()."""
+    """w: an sfm_qweight ([3D][D]), as made by qweight(): FP8 (a: E4M3 codes, a_scale: row
+    scales) or NF4 (a: bf16, a_scale: None)."""
     keep, p = _lens(text_lens) if text_lens is not None else (None, None)
     _check(lib().sfm_qkv_rope(ctx.handle, _ptr(a), _ptr(a_scale), ctypes.byref(w), _ptr(q_norm), _ptr(k_norm), _ptr(q),
                               _ptr(k), _ptr(vt), B, T, gh, gw, p, _stream(stream)))

@@ -394,30 +394,39 @@ def _bf16_place_apart(tag, a, b):
     return r <= 1.0
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "nf4"])
 @pytest.mark.parametrize("dims,B,T,gh,gw,lens", [("tiny", 1, 16, 16, 16, None), ("tiny", 2, 7, 16, 17, None),
                                                  ("tiny", 2, 16, 16, 16, [16, 5]),
                                                  ("ideogram4", 1, 512, 64, 64, None)])
-def test_qkv_rope_equals_separate_kernels(sfm, ctx_tiny, ctx_full, dims, B, T, gh, gw, lens):
+def test_qkv_rope_equals_separate_kernels(sfm, ctx_tiny, ctx_full, dims, B, T, gh, gw, lens, fmt):
     """The QKV projection with QK-norm and rotary in its epilogue against the STORE
-    projection followed by the rotary kernel, on the same codes: V^T bit for bit,
-    q and k within one bf16 place (the row's sum of squares adds in another order),
-    padding zero over NaN-filled outputs; samples whose rows start at no multiple of
-    32 (B 2, L 279) take the element-wise V^T stores."""
-    _say("qkv_rope", dims, B, T, gh, gw, lens)
+    projection followed by the rotary kernel, on the same operands (FP8: E4M3 codes
+    and row scales; NF4: a bf16 activation): V^T bit for bit, q and k within one
+    bf16 place (the row's sum of squares adds in another order), padding zero over
+    NaN-filled outputs; samples whose rows start at no multiple of 32 (B 2, L 279)
+    take the element-wise V^T stores."""
+    _say("qkv_rope", fmt, dims, B, T, gh, gw, lens)
     ctx = ctx_tiny if dims == "tiny" else ctx_full
     dm = O.TINY if dims == "tiny" else O.IDEOGRAM4
     H, D = dm.num_heads, dm.emb_dim
     L = T + gh * gw
     M = B * L
     Lp = sfm.sfm_padded_len(L)
-    a = _rand_codes((M, D), ("qa", dims, B, T))
-    sa = (torch.rand(M, generator=torch.Generator().manual_seed(3)) * 0.004 + 1e-3).float()
-    wq, ws = synth.fp8_weight(3 * D, D, ("qw", dims))
-    keep = (wq.to(DEV), ws.to(DEV))
-    w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    if fmt == "fp8":
+        a = _rand_codes((M, D), ("qa", dims, B, T))
+        sa = (torch.rand(M, generator=torch.Generator().manual_seed(3)) * 0.004 + 1e-3).float()
+        wq, ws = synth.fp8_weight(3 * D, D, ("qw", dims))
+        keep = (wq.to(DEV), ws.to(DEV))
+        w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+    else:
+        a = synth.bf16_normal((M, D), ("qa_nf4", dims, B, T), 1.0)
+        sa = None
+        wq, am = synth.nf4_weight(3 * D, D, ("qw_nf4", dims))
+        keep = (wq.to(DEV), am.to(DEV))
+        w = sfm.qweight(sfm.SFM_W_NF4_B64, *keep)
     qn = synth.bf16_normal((256,), ("qn2",), 0.02, 1.0).to(DEV)
     kn = synth.bf16_normal((256,), ("kn2",), 0.02, 1.0).to(DEV)
-    ad, sad = a.to(DEV), sa.to(DEV)
+    ad, sad = a.to(DEV), (sa.to(DEV) if sa is not None else None)
     outs = []
     for fused in (False, True):
         q = torch.full((B, H, Lp, 256), float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -438,8 +447,8 @@ def test_qkv_rope_equals_separate_kernels(sfm, ctx_tiny, ctx_full, dims, B, T, g
     assert torch.equal(v0, v1)
     for name, x0, x1 in (("q", q0, q1), ("k", k0, k1)):
         assert not torch.isnan(x1).any()
-        assert _bf16_place_apart(f"qkv_rope {dims} {B} {L} {name}", x0, x1)
-        check_rel(f"qkv_rope {dims} {B} {L} {name}", np64(x1), np64(x0), 1e-3)
+        assert _bf16_place_apart(f"qkv_rope {fmt} {dims} {B} {L} {name}", x0, x1)
+        check_rel(f"qkv_rope {fmt} {dims} {B} {L} {name}", np64(x1), np64(x0), 1e-3)
     assert torch.all(q1[:, :, L:] == 0) and torch.all(k1[:, :, L:] == 0)
 
 
