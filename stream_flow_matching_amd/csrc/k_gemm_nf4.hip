@@ -75,6 +75,22 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, SFM_LDS(lds), 16, voff, soff, 0, 0);
 }
 
+// 8 x byte E of w (the byte offset of its entry in the pair table) in one instruction: a
+// shift whose source operand selects the byte (SDWA), in place of a bit-field extract and a shift
+template <int E>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t w) {
+    uint32_t r;
+    if constexpr (E == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (E == 1)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (E == 2)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_nf4_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wq, const float* __restrict__ absmax, Nf4Code code,
@@ -102,7 +118,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(1024))) uint8_t ring_a1[BM * kRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t ring_b0[BN * kRowB];
     __shared__ __attribute__((aligned(1024))) uint8_t ring_b1[BN * kRowB];
-    __shared__ float2 lut2[256];
+    // (the table's alignment, the largest, puts it at LDS address 0: a lookup address is then the
+    // byte offset alone, with no base to add)
+    __shared__ __attribute__((aligned(2048))) float2 lut2[256];
     __shared__ float scl_lds[BM + 4 * BN];
     auto stage_a = [&](int s) -> uint8_t* { return s ? ring_a1 : ring_a0; };
     auto stage_b = [&](int s) -> uint8_t* { return s ? ring_b1 : ring_b0; };
@@ -173,8 +191,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint32_t ob[EPP / 8][4];
     auto lookup_c = [&](int slot, int p, int c) {
         const uint32_t w = nb[slot][p * (EPP / 8) + c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cvp[4 * c + e] = lut2[__builtin_amdgcn_ubfe(w, 8 * e, 8)];
+        const uint8_t* const t = reinterpret_cast<const uint8_t*>(lut2);
+        cvp[4 * c + 0] = *reinterpret_cast<const float2*>(t + byte_x8<0>(w));
+        cvp[4 * c + 1] = *reinterpret_cast<const float2*>(t + byte_x8<1>(w));
+        cvp[4 * c + 2] = *reinterpret_cast<const float2*>(t + byte_x8<2>(w));
+        cvp[4 * c + 3] = *reinterpret_cast<const float2*>(t + byte_x8<3>(w));
     };
     auto finish_k = [&](int slot, int stg, int p, int k) {
         const int c = k >> 1, h = k & 1;
