@@ -3,9 +3,10 @@
 // Research note, "Model architecture": one shared bidirectional self-attention
 // over the whole [text | image] sequence.  o = softmax(q k^T / 16) v per head.
 //
-// Layout: a workgroup owns 128 queries of one (batch, head); each of its eight
-// waves owns 16 queries whose q fragments stay in registers (two waves per SIMD,
-// at most 256 registers each).  Tiles of 64 keys stream global -> LDS with
+// Layout: a workgroup owns 192 queries of one (batch, head); each of its twelve
+// waves owns 16 queries whose q fragments stay in registers (three waves per
+// SIMD, at most 168 registers each: while one wave is in its softmax, two can
+// feed the SIMD's matrix core).  Tiles of 64 keys stream global -> LDS with
 // buffer_load ... lds (no staging registers): K as [key][d] and V^T as
 // [d][key], two stages of 64 KiB, one barrier per tile.  A wave raises its
 // priority while it issues matrix-core work and drops it for the softmax, so
@@ -30,7 +31,7 @@
 // which the per-token FP8 quantisation of o downstream turns into
 // percent-level changes of the block.
 //
-// Schedule: the work is the list of items (batch, head, block of 128 queries),
+// Schedule: the work is the list of items (batch, head, block of 192 queries),
 // batch-major, each with its walk of key tiles.  The grid is one persistent
 // workgroup per compute unit (G).  Workgroup g first takes whole items
 // r G + g for the R = items / G full rounds, so the workgroups of one XCD walk
@@ -68,7 +69,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define SFM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kQB = 128;              // queries per workgroup
+constexpr int kQB = 192;              // queries per workgroup
+constexpr int kWaves = kQB / 16;      // one wave per 16 queries
 constexpr int kKB = 64;               // keys per tile
 constexpr int kD = 256;
 constexpr int kKTile = kKB * kD * 2;  // 32 KiB
@@ -76,21 +78,24 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 struct Loader {
     __amdgpu_buffer_rsrc_t rk, rv;
-    uint32_t kvoff;         // per-lane byte offset inside a K tile
+    // a tile is 32 wave-loads of K and 32 of V^T (1 KiB each); wave w issues blocks w + 12 i
+    uint32_t kvoff[3];      // per-lane byte offsets inside a K tile, block wave + 12 i
     uint32_t vvoff;         // per-lane byte offset inside a V^T tile
     uint32_t lds0;          // this wave's first 1 KiB destination inside a tile
     int Lp2;                // bytes per V^T row
+    int nblk;               // 3 for waves 0..7, 2 for waves 8..11 (32 blocks per tile)
 
-    // 8 wave-level loads: 4 for the K tile (2 rows each), 4 for the V^T tile (8 rows each)
     __device__ __forceinline__ void issue(uint8_t* stage, int key0) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, SFM_LDS(stage + lds0 + i * 8192), 16, kvoff,
-                                                     (uint32_t)(key0 + 16 * i) * 512u, 0, 0);
+        for (int i = 0; i < 3; ++i)
+            if (i < nblk)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, SFM_LDS(stage + lds0 + i * 12288), 16, kvoff[i],
+                                                         (uint32_t)(key0 + 24 * i) * 512u, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, SFM_LDS(stage + kKTile + lds0 + i * 8192), 16, vvoff,
-                                                     (uint32_t)(64 * i * Lp2 + key0 * 2), 0, 0);
+        for (int i = 0; i < 3; ++i)
+            if (i < nblk)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, SFM_LDS(stage + kKTile + lds0 + i * 12288), 16, vvoff,
+                                                         (uint32_t)(96 * i * Lp2 + key0 * 2), 0, 0);
     }
 };
 
@@ -119,8 +124,8 @@ struct KeyWalk {
 // most max |v|, and fp16 keeps 3 more bits than the bf16 output), then (m, l) of its 16
 // queries in fp32; two slots per workgroup (the piece that starts inside an item, the piece
 // that ends inside one).  Sizes in floats.
-constexpr int kPartO = 8 * 16 * 64 * 2;
-constexpr int kPartFloats = kPartO + 8 * 16 * 2;
+constexpr int kPartO = kWaves * 16 * 64 * 2;
+constexpr int kPartFloats = kPartO + kWaves * 16 * 2;
 
 // Tail unit u (units counted from the first tile of item I0; items numbered batch-major, Hn per
 // batch): the item holding it, as batch b and item index it inside the batch, and the item's
@@ -146,7 +151,7 @@ __host__ __device__ __forceinline__ UnitPos locate_tail(int64_t u, int I0, int H
     }
 }
 
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(
+__global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     uint16_t* __restrict__ o, float* __restrict__ part, int L, int Lp, int H, int nqb, int T, TextLens lens,
     int varlen, int R, int64_t Ut) {
@@ -218,19 +223,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ld.Lp2 = Lp * 2;
         ld.lds0 = (uint32_t)wave * 1024;
         {
-            // K tile: 1 KiB block (wave + 8i) holds rows r = 2 wave + (lane >> 5) + 16 i (relative to the
-            // tile), physical chunk lane & 31 = logical chunk ^ (r & 15), which does not depend on i
-            {
+            // K tile: 1 KiB block (wave + 12 i) holds rows 2 wave + (lane >> 5) + 24 i (relative to the
+            // tile), physical chunk lane & 31 = logical chunk ^ (row & 15)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
                 const int r = 2 * wave + (lane >> 5);
-                ld.kvoff = (uint32_t)(r * 512 + (((lane & 31) ^ (r & 15)) * 16));
+                ld.kvoff[i] = (uint32_t)(r * 512 + (((lane & 31) ^ ((r + 24 * i) & 15)) * 16));
             }
-            // V^T tile: 1 KiB block (wave + 8i) holds rows 8 wave + (lane >> 3) + 64 i, physical chunk lane & 7
-            // = logical chunk ^ ((row >> 1) & 7) = logical ^ ((4 (wave & 1) + (lane >> 4)) & 7)
+            ld.nblk = wave < 8 ? 3 : 2;
+            // V^T tile: 1 KiB block (wave + 12 i) holds rows 8 wave + (lane >> 3) + 96 i, physical chunk
+            // lane & 7 = logical chunk ^ ((row >> 1) & 7) = logical ^ ((4 (wave & 1) + (lane >> 4)) & 7),
+            // which does not depend on i
             const int vrow = 8 * wave + (lane >> 3);
             ld.vvoff = (uint32_t)(vrow * Lp * 2 + (((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) * 16));
         }
 
-        // q fragments (B operand of S^T): rows q0 + qt*16 + lr, dims ks*32 + 8*lg .. +8
+        // q fragments (B operand of S^T): rows q0 + qt*16 + lr, dims ks*32 + 8*lg .. +8 (the last item's
+        // rows past Lp read row Lp - 1; their results are not stored)
         constexpr int NQT = 1;
         bf16x8 qf[NQT][8];
 #pragma unroll
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
                 qf[qt][ks] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(Qh + (int64_t)(q0 + qt * 16 + lr) * kD + ks * 32 + 8 * lg));
+                    bf16x8, *reinterpret_cast<const u32x4*>(Qh + (int64_t)min(q0 + qt * 16 + lr, Lp - 1) * kD + ks * 32 + 8 * lg));
 
         v4f oacc[NQT][16];
 #pragma unroll
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int qt = 0; qt < NQT; ++qt)
     #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4) s[qt][t4] = v4f{0.f, 0.f, 0.f, 0.f};
-            bf16x8 kf[3][4];
+            bf16x8 kf[2][4];
             auto load_kf = [&](int slot, int ks) {
                 const int base = kb[ks & 3] + (ks >> 2) * 256;
     #pragma unroll
@@ -268,16 +277,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             };
             __builtin_amdgcn_s_setprio(1);
             load_kf(0, 0);
-            load_kf(1, 1);
     #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
-                if (ks + 2 < 8) load_kf((ks + 2) % 3, ks + 2);
+                if (ks + 1 < 8) load_kf((ks + 1) & 1, ks + 1);
     #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4)
     #pragma unroll
                     for (int qt = 0; qt < NQT; ++qt)
                         s[qt][t4] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks % 3][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks & 1][t4], qf[qt][ks], s[qt][t4], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // mask keys >= L (ragged last tile) and the sample's text padding [Tb, T)
@@ -328,9 +336,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
 
-            // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments two groups of four
-            // d-tiles ahead (three register slots), like the K fragments of S^T (two steps ahead)
-            f16x8 vf[3][4];
+            // O^T[d][query] += sum_key V^T[d][key] P^T[key][query]; V^T fragments one group of four
+            // d-tiles ahead (two register slots), like the K fragments of S^T (one step ahead)
+            f16x8 vf[2][4];
             auto load_vf = [&](int slot, int g) {  // g = 0..7: h2 = g >> 2, d-tiles 4 (g & 3) .. +3
                 const int base = (g >> 2) ? vb1 : vb0;
     #pragma unroll
@@ -340,10 +348,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             };
             __builtin_amdgcn_s_setprio(1);
             load_vf(0, 0);
-            load_vf(1, 1);
     #pragma unroll
             for (int g = 0; g < 8; ++g) {
-                if (g + 2 < 8) load_vf((g + 2) % 3, g + 2);
+                if (g + 1 < 8) load_vf((g + 1) & 1, g + 1);
                 const int h2 = g >> 2;
     #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     #pragma unroll
                     for (int qt = 0; qt < NQT; ++qt)
                         oacc[qt][dt] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g % 3][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
+                            __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[g & 1][u], pf[qt][h2], oacc[qt][dt], 0, 0, 0);
                 }
                 if ((g & 3) == 3)
     #pragma unroll
@@ -519,13 +526,14 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     if (L == 0) return hipSuccess;
     if (grid < 0 || grid > kAttnMaxGrid) return hipErrorInvalidValue;
     const int Lp = padded_len(L);
-    const int nqb = Lp / kQB;
+    const int nqb = (L + kQB - 1) / kQB;
+
     TextLens tl{};
     if (lens) tl = *lens;
     const int Hn = H * nqb, items = B * Hn;
     if (grid == 0) {
         // one workgroup per item (no pieces)
-        hipLaunchKernelGGL(attn_kernel, dim3(items), dim3(512), 0, st, q, k, vt, o, part, L, Lp, H, nqb, T, tl,
+        hipLaunchKernelGGL(attn_kernel, dim3(items), dim3(64 * kWaves), 0, st, q, k, vt, o, part, L, Lp, H, nqb, T, tl,
                            lens ? 1 : 0, 1, (int64_t)0);
         return hipGetLastError();
     }
@@ -536,7 +544,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
     for (int b = I0 / Hn; b < B; ++b)
         Ut += (int64_t)(b == I0 / Hn ? (b + 1) * Hn - I0 : Hn) * KeyWalk(L, T, lens ? tl.len[b] : T).nkt;
     const int G = R > 0 ? grid : (int)std::min<int64_t>(grid, Ut);
-    hipLaunchKernelGGL(attn_kernel, dim3(G), dim3(512), 0, st, q, k, vt, o, part, L, Lp, H, nqb, T, tl, lens ? 1 : 0,
+    hipLaunchKernelGGL(attn_kernel, dim3(G), dim3(64 * kWaves), 0, st, q, k, vt, o, part, L, Lp, H, nqb, T, tl, lens ? 1 : 0,
                        R, Ut);
     if (G > 1 && Ut > 0) {
         MergeList ml;
@@ -544,7 +552,7 @@ hipError_t launch_attention(const uint16_t* q, const uint16_t* k, const uint16_t
         for (int j = 1; j < G; ++j)
             if (merges_at(j, G, R, Ut, Hn, L, T, tl, lens ? 1 : 0)) ml.j[nm++] = (uint16_t)j;
         if (nm > 0)
-            hipLaunchKernelGGL(attn_merge_kernel, dim3(nm, 8), dim3(64), 0, st, part, o, L, H, nqb, T, tl,
+            hipLaunchKernelGGL(attn_merge_kernel, dim3(nm, kWaves), dim3(64), 0, st, part, o, L, H, nqb, T, tl,
                                lens ? 1 : 0, R, Ut, G, ml);
     }
     return hipGetLastError();
