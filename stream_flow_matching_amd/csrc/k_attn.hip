@@ -371,6 +371,9 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // Two LDS stages: tile e0 + t lives in stage t & 1; the loads of tile t + 1 run during the
         // compute of tile t; one barrier per tile.
         const int n = e1 - e0;
+        // a wave whose 16 queries all lie past L (the last block when L is no multiple of 192) still
+        // issues its share of the loads and meets every barrier, but computes nothing
+        const bool active = q0 < L;
         ld.issue(st0, kw.key(e0));
         // the q fragments must have arrived here, before the barrier (otherwise the compiler moves
         // their loads behind it and the two latencies add up)
@@ -380,12 +383,12 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         __syncthreads();
         for (int t = 0; t < n; t += 2) {
             if (t + 1 < n) ld.issue(st1, kw.key(e0 + t + 1));
-            compute(st0, kw.key(e0 + t));
+            if (active) compute(st0, kw.key(e0 + t));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (t + 1 >= n) break;
             if (t + 2 < n) ld.issue(st0, kw.key(e0 + t + 2));
-            compute(st1, kw.key(e0 + t + 1));
+            if (active) compute(st1, kw.key(e0 + t + 1));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
