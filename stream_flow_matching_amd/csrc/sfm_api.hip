@@ -337,12 +337,13 @@ int run_block(const sfm_context* ctx, const sfm_block_weights* w, int fmt, const
         SFM_TIMED(launch_gemm_fp8_qkv_rope(b.hq, b.hs, (const uint8_t*)w->qkv.q, (const float*)w->qkv.scale, M, D, L,
                                            ra, st));
     } else {
-        // NF4: the same fused epilogue on the bf16-operand GEMM
+        // NF4: the STORE projection and the separate rotary kernel.  The fused epilogue
+        // (launch_gemm_nf4_qkv_rope, behind sfm_qkv_rope) is faster alone but measured slower
+        // inside the block (6.9 vs 6.7 ms per 6:1 NF4 block)
         SFM_LAUNCH(launch_adaln_bf16(x_in, L, 0, L, mod, ms, b.h, B, D, d->eps, st));
-        SFM_LAUNCH(launch_attn_pad_zero(b.q, b.k, b.vt, B, L, H, st));
-        const RopeArgs ra = rope_args(ctx, w->q_norm, w->k_norm, b.q, b.k, b.vt, T, gw, L, lens);
-        SFM_TIMED(launch_gemm_nf4_qkv_rope(b.h, (const uint8_t*)w->qkv.q, (const float*)w->qkv.scale, nf4_code(ctx), M, D,
-                                           L, ra, st));
+        SFM_TIMED(gemm(ctx, SFM_EPI_STORE, b.h, nullptr, &w->qkv, b.qkv, nullptr, nullptr, 0, M, L, st));
+        SFM_LAUNCH(launch_qk_norm_rope(b.qkv, w->q_norm, w->k_norm, ctx->rope_cos, ctx->rope_sin, b.q, b.k, b.vt, B, T,
+                                       gh, gw, H, d->eps, lens, st));
     }
     SFM_TIMED(launch_attention(b.q, b.k, b.vt, b.o, B, L, H, T, lens, b.part, shared ? 0 : ctx->attn_grid, st));
     uint16_t* s = b.qkv;  // qkv is dead after the rotary step
