@@ -10,8 +10,8 @@
 // buffer_load ... lds (no staging registers): K as [key][d] and V^T as
 // [d][key], two stages of 64 KiB, one barrier per tile.  A wave raises its
 // priority while it issues matrix-core work and drops it for the softmax, so
-// the SIMD's other wave, when it is in its MFMA sections, goes first and the
-// softmax arithmetic fills the gaps.
+// the SIMD's other waves, when they are in their MFMA sections, go first and
+// the softmax arithmetic fills the gaps.
 // Per tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K
 // rows, B = Q rows), so every lane holds the scores of ONE query column
 // (lane & 15) for keys 4*(lane>>4)+r: the softmax max is a reduction over the
@@ -21,7 +21,7 @@
 // registers as the B operand, and O^T's query column is again lane-local, so
 // rescaling is lane-local too.  The running max is only moved when a tile
 // raises it by more than 2^8 (scores then stay below 2^8 relative to the kept
-// max), which skips most rescales of the 128-register accumulator.
+// max), which skips most rescales of the 64-register accumulator.
 //
 // The P V product runs in fp16 (P and V^T in fp16, fp32 accumulation): fp16
 // keeps 3 more mantissa bits of P than bf16.  V's bf16 values are exact in
