@@ -19,7 +19,9 @@ constexpr int kEpiQkvRope = 4;
 // column 32 j + 8 (r >> 2) + 4 (l >> 5) + (r & 3), as in gemm_epilogue_lds) of a 256 x 256 tile
 // of the QKV output: with 256-column tiles, tile column tn is head tn % H of q, k or v
 // (part tn / H), and the wave holds columns wn 128 .. wn 128 + 127 of that head.  Every value
-// is first rounded to bf16 (the projection's output precision).
+// is first rounded to bf16 (the projection's output precision).  gml: the tile's gamma (q_norm
+// for q tiles, k_norm for k tiles) as 128 packed bf16 pairs in LDS, loaded by the kernel at its
+// start (load_qk_gamma).
 //   q, k: the row's sum of squares over the head (the lane, its partner lane l ^ 32, then the
 //     other column wave through `xch` in LDS), u / sqrt(mean(u^2) + eps) * gamma, and for the
 //     dims j < 64 / j + 64 of wave 0 the rotation of pair j (the partner of fragment column j
@@ -30,10 +32,18 @@ constexpr int kEpiQkvRope = 4;
 //     order of vt_slot and stored as 16-byte chunks of V^T[b][h][d][l] when the wave's rows are
 //     128 valid rows of one sample starting at a multiple of 32 of its sequence; otherwise each
 //     value is stored on its own.
+// The kernel prologue's part of the epilogue: thread tid < 128 loads dword tid of the gamma of
+// tile column tn's part (q_norm for q heads, k_norm for k heads; none for v) for gml.
+__device__ __forceinline__ uint32_t load_qk_gamma(const RopeArgs& ra, int tn, int tid) {
+    const int part = tn / ra.H;
+    if (part >= 2 || tid >= 128) return 0u;
+    return reinterpret_cast<const uint32_t*>(part == 0 ? ra.qn : ra.kn)[tid];
+}
+
 template <int FM, int FN>
 __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uint8_t* lds, float* xch, int m0w,
                                                   int wm, int wn, int tn, int lane, int M, int L, const float* rsl,
-                                                  const float* csl, const RopeArgs& ra) {
+                                                  const float* csl, const uint32_t* gml, const RopeArgs& ra) {
     constexpr int TM = 32 * FM, TN = 32 * FN;
     static_assert(TM == 128 && TN == 128, "a 256 x 256 tile: one head per tile column");
     const int lc = lane & 31, lg = lane >> 5;
@@ -53,6 +63,32 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
     // the wave's rows span at most two samples (L >= 256 > TM)
     const int b_first = min(m0w, M - 1) / L, split = (b_first + 1) * L;
     if (part < 2) {
+        // the rows' positions on the three axes and the first column group's cos / sin (wave 0
+        // rotates), ahead of the sums of squares so that the loads' latency runs under them
+        int pax[FM][3];
+        if (wn == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = min(m0w + 32 * i + lc, M - 1);
+                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
+                const int Tb = ra.varlen ? ra.lens.len[b] : ra.T;
+#pragma unroll
+                for (int a = 0; a < 3; ++a) pax[i][a] = axis_pos(l, ra.T, Tb, ra.gw, a);
+            }
+        }
+        // wave 0: cos / sin of the four rows for column group g = 4 j + q (pairs p0 .. p0 + 3, which
+        // share an axis: the section boundaries 24 and 44 are multiples of 4), one group ahead
+        v4f c2[2][FM], s2[2][FM];
+        auto load_cs = [&](int slot, int g) {
+            const int p0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * lg;
+            const int ax = p0 < 24 ? 0 : (p0 < 44 ? 1 : 2);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                c2[slot][i] = *reinterpret_cast<const v4f*>(ra.cos_t + pax[i][ax] * 64 + p0);
+                s2[slot][i] = *reinterpret_cast<const v4f*>(ra.sin_t + pax[i][ax] * 64 + p0);
+            }
+        };
+        if (wn == 0) load_cs(0, 0);
         float rn[FM] = {};
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -75,21 +111,9 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             rn[i] = 1.0f / sqrtf((rn[i] + xch[(2 * wm + (wn ^ 1)) * TM + 32 * i + lc]) / 256.0f + ra.eps);
-        // the rows' positions on the three axes (wave 0 rotates)
-        int pax[FM][3];
-        if (wn == 0) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int m = min(m0w + 32 * i + lc, M - 1);
-                const int b = m < split ? b_first : b_first + 1, l = m - b * L;
-                const int Tb = ra.varlen ? ra.lens.len[b] : ra.T;
-#pragma unroll
-                for (int a = 0; a < 3; ++a) pax[i][a] = axis_pos(l, ra.T, Tb, ra.gw, a);
-            }
-        }
-        const uint16_t* gam = (part == 0 ? ra.qn : ra.kn) + wn * TN;
+        // gamma (q_norm or k_norm of the tile's part) from LDS, where the kernel put it at its start
         auto gamma4 = [&](int j, int q) {
-            const uint2 g2 = *reinterpret_cast<const uint2*>(gam + 32 * j + 8 * q + 4 * lg);
+            const uint2 g2 = *reinterpret_cast<const uint2*>(gml + (wn * TN + 32 * j + 8 * q + 4 * lg) / 2);
             return v4f{__uint_as_float(g2.x << 16), __uint_as_float(g2.x & 0xFFFF0000u), __uint_as_float(g2.y << 16),
                        __uint_as_float(g2.y & 0xFFFF0000u)};
         };
@@ -98,19 +122,6 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
             *reinterpret_cast<uint2*>(lds + row * 256 + ((ch ^ (row & 15)) << 4) + lg * 8) =
                 make_uint2(cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]));
         };
-        // wave 0: cos / sin of the four rows for column group g = 4 j + q (pairs p0 .. p0 + 3, which
-        // share an axis: the section boundaries 24 and 44 are multiples of 4), one group ahead
-        v4f c2[2][FM], s2[2][FM];
-        auto load_cs = [&](int slot, int g) {
-            const int p0 = 32 * (g >> 2) + 8 * (g & 3) + 4 * lg;
-            const int ax = p0 < 24 ? 0 : (p0 < 44 ? 1 : 2);
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                c2[slot][i] = *reinterpret_cast<const v4f*>(ra.cos_t + pax[i][ax] * 64 + p0);
-                s2[slot][i] = *reinterpret_cast<const v4f*>(ra.sin_t + pax[i][ax] * 64 + p0);
-            }
-        };
-        if (wn == 0) load_cs(0, 0);
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j)
 #pragma unroll

@@ -271,6 +271,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         scv[k] = v;
     }
 
+    uint32_t qk_gamma = 0u;
+    if constexpr (EPI == kEpiQkvRope) qk_gamma = load_qk_gamma(rope, tn, tid);
+
     // K % 256 == 0 (checked by the caller) and klen a multiple of 256: nks >= 2 and even
     const int nks = klen / kBK;
     if constexpr (MX) load_exp(su, 0);
@@ -286,6 +289,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int k = 0; k < NSL; ++k)
         if (tid + 256 * k < NSC) scl[tid + 256 * k] = scv[k];
+    // the QK-norm gamma of the tile's part behind the row-sum exchange area of the epilogue
+    if constexpr (EPI == kEpiQkvRope)
+        if (tid < 128) reinterpret_cast<uint32_t*>(scl + BM + BN + 4 * TM)[tid] = qk_gamma;
     lds_barrier();
     // in program order, as the loop reads them: the loop head then waits only for the first
     // fragments (issued in another order, the first MFMA would need the last read and the
@@ -349,7 +355,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else if constexpr (EPI == kEpiQkvRope) {
         // the gate area behind the scales (unused by this epilogue) takes the row sums of squares
         epilogue_qkv_rope<FM, FN>(acc, smem + wave * (Lds::RING / 4), scl + BM + BN, m0 + wm * TM, wm, wn, tn, lane, M,
-                                  L, scl + wm * TM, scl + BM + wn * TN, rope);
+                                  L, scl + wm * TM, scl + BM + wn * TN,
+                                  reinterpret_cast<const uint32_t*>(scl + BM + BN + 4 * TM), rope);
     } else {
         gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, smem + wave * (Lds::RING / 4), m0 + wm * TM, wn, tn, lane, M, N, L,
                                                out, resid, scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN,

@@ -146,6 +146,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         scl[e] = v;
     }
+    // the QK-norm gamma of the tile's part behind the row-sum exchange area of the epilogue
+    if constexpr (EPI == kEpiQkvRope)
+        if (tid < 128) reinterpret_cast<uint32_t*>(scl + BM + BN + 4 * TM)[tid] = load_qk_gamma(rope, tn, tid);
 
     // activation tile: wave-load v covers tile rows 8 (wave + 4 v) + (lane >> 3), physical chunk
     // lane & 7 holding logical chunk (lane & 7) ^ ((row >> 1) & 7)
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint8_t* const estg = wave == 0 ? ring_a0 : wave == 1 ? ring_b0 : wave == 2 ? ring_a1 : ring_b1;
     if constexpr (EPI == kEpiQkvRope)
         epilogue_qkv_rope<FM, FN>(acc, estg, scl + BM + BN, m0 + wm * TM, wm, wn, tn, lane, M, L, scl + wm * TM,
-                                  scl + BM + wn * TN, rope);
+                                  scl + BM + wn * TN, reinterpret_cast<const uint32_t*>(scl + BM + BN + 4 * TM), rope);
     else
         gemm_epilogue_lds<EPI, BN, TN, FM, FN>(acc, estg, m0 + wm * TM, wn, tn, lane, M, N, L, out, resid,
                                                  scl + wm * TM, scl + BM + wn * TN, scl + BM + BN + wn * TN, bt0);
