@@ -641,6 +641,29 @@ def test_block_full_sampled(sfm, ctx_full, name):
     check_rel("test_block_full_sampled#2", got - xin, ref - xin, UPDATE_BAR[w.wfmt])
 
 
+@pytest.mark.parametrize("T", [0, 404])
+def test_block_full_other_lengths(sfm, ctx_full, T):
+    """Full-width FP8 blocks at the image-only pass's length (no text, M 4096)
+    and at 404 text tokens (M 4500: the last row of 256 x 256 tiles partly
+    filled, the text/image boundary inside a tile), sampled rows against the
+    oracle, including rows of the last tile row."""
+    _say("block full, T", T)
+    w = synth.Workload(f"block_full_T{T}", synth.FULL, 1, T, 64, 64)
+    p = synth.block_params(w.shape, (0, w.name), "fp8")
+    x, c = synth.block_inputs(w)
+    xo = _run_block(sfm, ctx_full, w, p, x, c)
+    M = w.B * w.L
+    # rows of whole tiles and of tail tiles (the last tile row), around the text/image boundary
+    rows = np.unique(np.r_[0, 255, 256, max(T - 1, 0), T, 3839, 3840, M - 257, M - 1,
+                           np.linspace(0, M - 1, 9).astype(int)])
+    ref = O.block_forward(np64(x), c.numpy().astype(np.float64), oracle_block(p), w.T, w.gh, w.gw, O.IDEOGRAM4,
+                          rows=rows)
+    got = np64(xo).reshape(M, -1)[rows]
+    xin = np64(x).reshape(M, -1)[rows]
+    check_rel(f"test_block_full_other_lengths[{T}]#1", got, ref, 1e-2)
+    check_rel(f"test_block_full_other_lengths[{T}]#2", got - xin, ref - xin, UPDATE_BAR["fp8"])
+
+
 def test_block_deterministic(sfm, ctx_full):
     _say("block determinism")
     w = synth.WORKLOADS["block_1024"]
@@ -652,15 +675,26 @@ def test_block_deterministic(sfm, ctx_full):
     assert torch.isfinite(a.float()).all()
 
 
-@pytest.mark.parametrize("what", ["block_fp8", "block_nf4", "step"])
-def test_poisoned_workspace_changes_nothing(sfm, ctx_tiny, what):
+@pytest.mark.parametrize("what", ["block_fp8", "block_nf4", "step", "block_fp8_full"])
+def test_poisoned_workspace_changes_nothing(sfm, ctx_tiny, ctx_full, what):
     """The workspace is filled with 0xFF bytes (NaN as fp32, bf16 and fp16)
     before the call: the output equals the call on a zeroed workspace bitwise,
-    so no kernel reads workspace it has not written first."""
+    so no kernel reads workspace it has not written first (tiny shapes, and the
+    full-width 1024^2 block with its persistent attention grid and merge)."""
     _say("poisoned workspace", what)
     w = synth.Workload("tiny_poison", synth.TINY, 2, 16, 16, 16, layers=2)
     outs = []
-    if what == "step":
+    if what == "block_fp8_full":
+        w = synth.WORKLOADS["block_1024"]
+        bw = sfm.BlockWeights(to_device(synth.block_params(w.shape, (0, "poison_full"), "fp8")))
+        x, c = synth.block_inputs(w, device=DEV)
+        for fill in (0, 255):
+            ws = sfm.workspace(sfm.sfm_block_workspace_bytes(ctx_full, 1, w.T, w.gh, w.gw, bw.fmt)).fill_(fill)
+            xo = torch.empty_like(x)
+            sfm.sfm_block_forward(ctx_full, bw, x, xo, c, 1, w.T, w.gh, w.gw, ws)
+            torch.cuda.synchronize()
+            outs.append(xo.float())
+    elif what == "step":
         cond = to_device(synth.model_params(w.shape, 2, (0, "poison_c")))
         unc = to_device(synth.model_params(w.shape, 2, (0, "poison_u")))
         cm, um = sfm.ModelWeights(cond), sfm.ModelWeights(unc)
