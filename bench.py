@@ -838,13 +838,39 @@ def cpu_baseline(sample):
         r["tokens_per_s" if rows is None else "rows_per_s"] = round(toks / sec, 2)
         return r
 
+    def fp32_products(name):
+        """The matrix products of one whole block in float32 (torch on the CPU, its own
+        threads): the QKV, output, gate/up and down projections on decoded weights and the
+        attention's two products per head, without the norms, softmax, rotary or
+        quantisation; a lower bound on the time of any float32 CPU block."""
+        import torch
+        w = synth.WORKLOADS[name]
+        d, f, L, H = w.shape.emb_dim, w.shape.intermediate, w.L, w.shape.emb_dim // 256
+        g = torch.Generator().manual_seed(0)
+        mk = lambda *s: torch.randn(*s, generator=g)
+        x, wqkv, wo, wgu, wd = mk(L, d), mk(d, 3 * d), mk(d, d), mk(d, 2 * f), mk(f, d)
+        q, k, v, s_, hh = mk(H, L, 256), mk(H, 256, L), mk(H, L, 256), mk(L, f), mk(L, d)
+        t0 = time.perf_counter()
+        torch.mm(x, wqkv)
+        for h in range(H):
+            torch.mm(torch.mm(q[h], k[h]), v[h])
+        torch.mm(hh, wo)
+        torch.mm(x, wgu)
+        torch.mm(s_, wd)
+        sec = time.perf_counter() - t0
+        flop = block_flops(L, 1, d, f)
+        return {"workload": name, "rows": "all", "s": round(sec, 2), "gflop_s": round(flop / sec / 1e9, 1),
+                "tokens_per_s": round(L / sec, 2), "threads": torch.get_num_threads(),
+                "what": "float32 matrix products only (torch CPU): a lower bound for a float32 CPU block"}
+
     main = run(sample)
     runs = [main, run("tiny_block"), run("block_2048", 16), run("block_6to1_nf4", 16)]
     model, blas, threads = cpu_info()
     return {"value": main["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"one whole block of {sample} ({main['s']} s, float64 oracle, weights decoded beforehand "
                       f"in {main['decode_s']} s)",
-            "cpu_model": model, "blas": blas, "precision": "float64", "runs": runs}
+            "cpu_model": model, "blas": blas, "precision": "float64", "runs": runs,
+            "fp32_products": fp32_products(sample)}
 
 
 def main():
