@@ -82,6 +82,65 @@ def time_gpu(fn, iters, warmup=1):
     return s.elapsed_time(e) / iters / 1e3   # seconds per call
 
 
+class ClockSampler:
+    """The GPU's gfx clock (the mean over its XCDs) and socket power, read from the
+    amdsmi GPU metrics every `period` seconds by a thread while a workload runs.
+    ok is False when amdsmi is missing or the device cannot be identified."""
+
+    def __init__(self, period=0.01):
+        import threading
+        self.ok, self.period, self.samples = False, period, []
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            self.smi = amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self.h = handles[0] if len(handles) == 1 else None
+            self.ok = self.h is not None
+        except Exception:
+            self.ok = False
+
+    def read(self):
+        m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        pw = m.get("current_socket_power")
+        return (float(clk) if isinstance(clk, (int, float)) else None,
+                float(pw) if isinstance(pw, (int, float)) else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read())
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+        return False
+
+    def summary(self, what):
+        import statistics
+        clk = sorted(c for c, _ in self.samples if c)
+        pw = sorted(p for _, p in self.samples if p)
+        if not clk:
+            return None
+        return {"mhz_median": round(statistics.median(clk), 1), "mhz_min": round(clk[0], 1),
+                "mhz_max": round(clk[-1], 1), "socket_power_w_median": round(statistics.median(pw), 1) if pw else None,
+                "samples": len(clk), "source": "amdsmi GPU metrics: current gfx clock of each XCD (mean over XCDs), "
+                                               f"read every {self.period * 1e3:.0f} ms during {what}"}
+
+
 def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
     """Times `steps` CFG steps between two synchronisations; the last timed step
     runs through sfm_cfg_step_timed, which records HIP events on the launch
@@ -115,6 +174,16 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
     us = [evb[i].elapsed_time(eve[i]) * 1e3 for i in range(rec)]   # microseconds
+    # the clock under this load: five more guided steps (outside the timed region) with the
+    # metrics read beside them
+    clock = None
+    sampler = ClockSampler()
+    if sampler.ok:
+        with sampler:
+            for _ in range(5):
+                step()
+            torch.cuda.synchronize()
+        clock = sampler.summary("five guided steps run right after the timed ones")
     nk = len(KINDS)
     # pair (p * layers + l) * 5 + j: pass p (0 conditional, 1 unconditional), layer l, launch j
     launches = {kind: [[us[(p * w.layers + l) * nk + j] for l in range(w.layers) if (p * w.layers + l) * nk + j < rec]
@@ -141,7 +210,7 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
                                            weights="QKV and output projection FP8, gate/up and down MXFP4")
         del mixed
     torch.cuda.empty_cache()
-    return sec, ok, launches, samples, streamed
+    return sec, ok, launches, samples, streamed, clock
 
 
 def streamed_bench(sfm, ctx, cond, cm, text, z, t, w, iters=2, weights="FP8"):
@@ -908,11 +977,15 @@ def main():
     w = synth.WORKLOADS["cfg_step_1024"]
     presets = () if args.no_extra else (("V4_TURBO_12", sfm.SFM_PRESET_V4_TURBO_12),
                                          ("V4_QUALITY_48", sfm.SFM_PRESET_V4_QUALITY_48))
-    sec, ok, launches, samples, streamed = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup, presets)
+    sec, ok, launches, samples, streamed, clock = cfg_step_bench(sfm, synth, ctx, args.steps, args.warmup, presets)
     tokens = w.layers * (w.B * (w.T + w.gh * w.gw) + w.B * w.gh * w.gw)
     flops = w.layers * (block_flops(w.T + w.gh * w.gw, w.B) + block_flops(w.gh * w.gw, w.B))
     step_tflops = flops / sec / 1e12
     roof = roofline(kernel_table(launches, w), w)
+    if clock:
+        # the same fraction against the matrix peak at the clock measured under this load
+        roof["peak_at_clock"] = round(roof["peak"] * clock["mhz_median"] / 2400.0, 1)
+        roof["frac_at_clock"] = round(roof["achieved"] / roof["peak_at_clock"], 4)
     hbm = None if args.no_hbm else hbm_kernels(sfm, synth, ctx)
     extra = {}
     if not args.no_extra:
@@ -946,6 +1019,7 @@ def main():
                    "image_grid": [w.gh, w.gw], "layers": w.layers, "weight_sets": 2, "guidance": 4.0,
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "gpu_clock": clock,
         "hbm_kernels": hbm,
         "cpu_baseline": cpu,
         "blocks": extra,
