@@ -129,10 +129,11 @@ class ClockSampler:
         self._thread.join()
         return False
 
-    def summary(self, what):
+    def summary(self, what, keep_last=1.0):
         import statistics
-        clk = sorted(c for c, _ in self.samples if c)
-        pw = sorted(p for _, p in self.samples if p)
+        kept = self.samples[int(len(self.samples) * (1.0 - keep_last)):]
+        clk = sorted(c for c, _ in kept if c)
+        pw = sorted(p for _, p in kept if p)
         if not clk:
             return None
         return {"mhz_median": round(statistics.median(clk), 1), "mhz_min": round(clk[0], 1),
@@ -167,6 +168,20 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the clock under this load: guided steps for about two seconds between the warm-up and
+    # the timed steps, with the metrics read beside them (the timed step with events stays the
+    # last); the metrics table refreshes far more slowly than it is read, so only the second
+    # second's readings count
+    clock = None
+    sampler = ClockSampler()
+    if sampler.ok:
+        with sampler:
+            t_end = time.perf_counter() + 2.0
+            while time.perf_counter() < t_end:
+                step()
+                torch.cuda.synchronize()
+        clock = sampler.summary("guided steps run for 2 s between the warm-up and the timed steps (readings of the "
+                                "second second)", keep_last=0.5)
     t0 = time.perf_counter()
     for _ in range(steps - 1):
         step()
@@ -174,16 +189,6 @@ def cfg_step_bench(sfm, synth, ctx, steps, warmup, presets=()):
     torch.cuda.synchronize()
     sec = (time.perf_counter() - t0) / steps
     us = [evb[i].elapsed_time(eve[i]) * 1e3 for i in range(rec)]   # microseconds
-    # the clock under this load: five more guided steps (outside the timed region) with the
-    # metrics read beside them
-    clock = None
-    sampler = ClockSampler()
-    if sampler.ok:
-        with sampler:
-            for _ in range(5):
-                step()
-            torch.cuda.synchronize()
-        clock = sampler.summary("five guided steps run right after the timed ones")
     nk = len(KINDS)
     # pair (p * layers + l) * 5 + j: pass p (0 conditional, 1 unconditional), layer l, launch j
     launches = {kind: [[us[(p * w.layers + l) * nk + j] for l in range(w.layers) if (p * w.layers + l) * nk + j < rec]

@@ -41,7 +41,7 @@ __device__ __forceinline__ uint32_t load_qk_gamma(const RopeArgs& ra, int tn, in
 }
 
 template <int FM, int FN>
-__device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uint8_t* lds, float* xch, int m0w,
+__device__ __forceinline__ void epilogue_qkv_rope(v16f (&acc)[FM][FN], uint8_t* lds, float* xch, int m0w,
                                                   int wm, int wn, int tn, int lane, int M, int L, const float* rsl,
                                                   const float* csl, const uint32_t* gml, const RopeArgs& ra) {
     constexpr int TM = 32 * FM, TN = 32 * FN;
@@ -89,6 +89,7 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
             }
         };
         if (wn == 0) load_cs(0, 0);
+        // the output values replace the accumulators, which the normalisation below reads back
         float rn[FM] = {};
 #pragma unroll
         for (int j = 0; j < FN; ++j)
@@ -99,7 +100,10 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
                 for (int i = 0; i < FM; ++i) {
                     const v4f u = y4(i, j, q, cs);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) rn[i] += u[e] * u[e];
+                    for (int e = 0; e < 4; ++e) {
+                        rn[i] += u[e] * u[e];
+                        acc[i][j][4 * q + e] = u[e];
+                    }
                 }
             }
 #pragma unroll
@@ -129,13 +133,17 @@ __device__ __forceinline__ void epilogue_qkv_rope(const v16f (&acc)[FM][FN], uin
                 // columns c (fragment column j) and c + 64 (fragment column j + 2)
                 const int g = 4 * j + q;
                 if (wn == 0 && g + 1 < 2 * FN) load_cs((g + 1) & 1, g + 1);
-                const v4f csa = colscale(j, q), csb = colscale(j + FN / 2, q);
                 const v4f ga = gamma4(j, q), gb = gamma4(j + FN / 2, q);
                 const v4f* c = c2[g & 1];
                 const v4f* sn = s2[g & 1];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
-                    v4f a = y4(i, j, q, csa), bb = y4(i, j + FN / 2, q, csb);
+                    v4f a, bb;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        a[e] = acc[i][j][4 * q + e];
+                        bb[e] = acc[i][j + FN / 2][4 * q + e];
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         a[e] = a[e] * rn[i] * ga[e];

@@ -191,6 +191,40 @@ def test_linear_fp8(sfm, ctx_tiny, epi, M):
         check_rel("test_linear_fp8#2", got - np64(resid), ref - np64(resid), 1e-2)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "nf4"])
+def test_empty_inputs_are_no_ops(sfm, ctx_tiny, fmt):
+    """Zero rows: the projection (each epilogue), the per-token quantisation and
+    the Euler update return success and leave their outputs untouched."""
+    _say("empty inputs", fmt)
+    K, Nw = 512, 1536
+    if fmt == "fp8":
+        keep = tuple(t.to(DEV) for t in synth.fp8_weight(Nw, K, ("ew",)))
+        w = sfm.qweight(sfm.SFM_W_FP8_E4M3, *keep)
+        a, sa = torch.zeros(16, K, dtype=torch.uint8, device=DEV), torch.ones(16, device=DEV)
+    else:
+        keep = tuple(t.to(DEV) for t in synth.nf4_weight(Nw, K, ("ew",)))
+        w = sfm.qweight(sfm.SFM_W_NF4_B64, *keep)
+        a, sa = torch.zeros(16, K, dtype=torch.bfloat16, device=DEV), None
+    resid = torch.zeros(16, Nw, dtype=torch.bfloat16, device=DEV)
+    gate = torch.ones(1, Nw, device=DEV)
+    for epi in (0, 1, 2):
+        out = torch.full((16, Nw), 7.0, dtype=torch.bfloat16, device=DEV)
+        sfm.sfm_linear(ctx_tiny, epi, a, sa, w, out, resid if epi == 1 else None, gate if epi == 1 else None, Nw,
+                       M=0, L=16)
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())
+    q = torch.full((16, K), 3, dtype=torch.uint8, device=DEV)
+    sc = torch.full((16,), 5.0, device=DEV)
+    src = torch.ones(16, K, dtype=torch.bfloat16, device=DEV)
+    assert sfm.lib().sfm_quant_rows_fp8(sfm._ptr(src), 0, K, sfm._ptr(q), sfm._ptr(sc), sfm._stream()) == 0
+    z = torch.ones(64, device=DEV)
+    zo = torch.full((64,), 9.0, device=DEV)
+    assert sfm.lib().sfm_euler_cfg(sfm._ptr(z), sfm._ptr(z), sfm._ptr(z), sfm._ptr(zo), None, 0, 4.0, 0.5,
+                                   sfm._stream()) == 0
+    torch.cuda.synchronize()
+    assert bool((q == 3).all()) and bool((sc == 5.0).all()) and bool((zo == 9.0).all())
+
+
 def test_linear_fp8_full_width_sampled(sfm, ctx_full):
     """QKV projection at the 1024^2 block shape (M 4608, N 13824, K 4608);
     sampled rows against the oracle."""
