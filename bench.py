@@ -127,6 +127,10 @@ class ClockSampler:
     def __exit__(self, *exc):
         self._stop.set()
         self._thread.join()
+        try:
+            self.smi.amdsmi_shut_down()
+        except Exception:
+            pass
         return False
 
     def summary(self, what, keep_last=1.0):
