@@ -19,7 +19,8 @@ constexpr int kEpiQkvRope = 4;
 // column 32 j + 8 (r >> 2) + 4 (l >> 5) + (r & 3), as in gemm_epilogue_lds) of a 256 x 256 tile
 // of the QKV output: with 256-column tiles, tile column tn is head tn % H of q, k or v
 // (part tn / H), and the wave holds columns wn 128 .. wn 128 + 127 of that head.  Every value
-// is first rounded to bf16 (the projection's output precision).  gml: the tile's gamma (q_norm
+// is first rounded to bf16 (the projection's output precision); for q and k these values
+// overwrite the accumulators, which the normalising pass then reads.  gml: the tile's gamma (q_norm
 // for q tiles, k_norm for k tiles) as 128 packed bf16 pairs in LDS, loaded by the kernel at its
 // start (load_qk_gamma).
 //   q, k: the row's sum of squares over the head (the lane, its partner lane l ^ 32, then the
