@@ -149,3 +149,18 @@ def test_one_gpu_guard():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_clock_summary_keeps_the_late_readings():
+    """The clock summary keeps the last fraction of the readings (the metrics table refreshes
+    slowly, so the first readings of a load can still hold the idle clock) and reports their
+    median, range and socket power; with no readings it reports nothing."""
+    cs = bench.ClockSampler.__new__(bench.ClockSampler)
+    cs.period = 0.01
+    cs.samples = [(150.0, 250.0)] * 6 + [(1800.0, 1380.0), (1850.0, 1390.0), (1840.0, None), (None, 1385.0)]
+    got = cs.summary("a test", keep_last=0.4)
+    assert got["mhz_median"] == 1840.0 and got["mhz_min"] == 1800.0 and got["mhz_max"] == 1850.0
+    assert got["socket_power_w_median"] == 1385.0 and got["samples"] == 3
+    assert bench.ClockSampler.summary(cs, "all", keep_last=1.0)["mhz_min"] == 150.0
+    cs.samples = []
+    assert cs.summary("nothing") is None
