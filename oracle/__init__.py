@@ -72,6 +72,8 @@ What pins each function (tests/test_oracle_numerics.py, tests/test_oracle_dit.py
   sampler presets        the research note's preset table (tests/golden)
   sampler.euler_loop / sample   constant velocity telescopes to z + v, the linear
                          ODE's product form, chaining of the guided steps
+tests/oracle_mutations.py plants 22 plausible single-line mistakes in a scratch copy of
+dit.py; each one fails at least one of the pins above.
 Parity unpinned: the whole model against a real checkpoint (none exists here).
 The modulation chunk order, the timestep MLP and the final layer are readings
 of prose: the pins fix that the oracle computes exactly those readings, not
